@@ -1,0 +1,243 @@
+"""Benchmark of the FP8 training hot path on one MI355X.
+
+One step is one pass of every stage of the path over one batch of synthetic
+input, in the shapes of the MLP up-projection of a 768-wide GPT at 64 x 1024
+tokens plus a fine-grained block-scaled projection:
+
+  forward   quantize X [65536,768] -> E4M3 (per-tensor amax scale, + X^T copy)
+            y  = X W^T            [65536,3072]   (W from the FP8 weight cache)
+  backward  quantize dY [65536,3072] -> E5M2 (per-tensor, + dY^T copy)
+            dX = dY W             [65536,768]    (E5M2 x E4M3, W^T cache copy)
+            dW = dY^T X           [3072,768]     (K = 65536, split K)
+  update    optimizer-side master change, then the weight-cache refresh
+            (amax + cast + transposed copy of W [3072,768])
+  fine      quantize A [16384,7168] in 1x128 row tiles, B [2048,7168] in
+            128x128 blocks, block-scaled GEMM [16384,2048]
+
+value = all GEMM flops of the step / step time (TFLOP/s, inputs resident in
+HBM).  Every stage's kernels are bracketed with HIP events inside the timed
+region, which gives each stage's average duration; the roofline entry uses
+the dominant kernel's.  The CPU oracle is timed on a bounded sample of the
+same work (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOP/s (% of FP8 MFMA peak) + quantize GB/s (% HBM)"
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+TOK, D, F = 65536, 768, 3072   # tokens, d_model, 4 d_model
+FA_M, FA_N, FA_K = 16384, 2048, 7168
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=32768)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU share is "
+              "the whole workload; see DESIGN.md for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_scaled_matmul_amd as fm
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.time()
+    x = to_dev(synth.normal_bf16(3, 0, (TOK, D), 1.0))
+    w_bits = synth.normal_bf16(3, 1, (F, D), 0.02)
+    w_master = to_dev(w_bits)
+    dy = to_dev(synth.normal_bf16(5, 0, (TOK, F), 1e-3))
+    a_fine = to_dev(synth.channel_scaled_bf16(4, 0, 3, (FA_M, FA_K)))
+    b_fine = to_dev(synth.channel_scaled_bf16(4, 1, 4, (FA_N, FA_K)))
+    noise = torch.from_numpy(synth.update_noise_f32(3, (F, D))).to(dev)
+    gen_s = time.time() - t_gen
+
+    # outputs and caches, allocated once
+    xq = torch.empty((TOK, D), dtype=torch.uint8, device=dev)
+    xqt = torch.empty((D, TOK), dtype=torch.uint8, device=dev)
+    xs = torch.empty(1, dtype=torch.float32, device=dev)
+    dyq = torch.empty((TOK, F), dtype=torch.uint8, device=dev)
+    dyqt = torch.empty((F, TOK), dtype=torch.uint8, device=dev)
+    dys = torch.empty(1, dtype=torch.float32, device=dev)
+    y = torch.empty((TOK, F), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((TOK, D), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((F, D), dtype=torch.bfloat16, device=dev)
+    aq = torch.empty((FA_M, FA_K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((FA_M, FA_K // 128), dtype=torch.float32, device=dev)
+    bq = torch.empty((FA_N, FA_K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((FA_N // 128, FA_K // 128), dtype=torch.float32, device=dev)
+    yf = torch.empty((FA_M, FA_N), dtype=torch.bfloat16, device=dev)
+    ctr = fm.Counters(dev)
+    cache = fm.WeightCache(F, D, fm.E4M3, fm.TENSOR, with_t=True, counters=ctr, device=dev)
+    fm.requant_weights([cache], [w_master])
+    dw_ws = torch.empty(max(fm.lib().fp8_scaled_mm_workspace_size(F, D, TOK, 0, 0), 1),
+                        dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    # (name, flops, algorithmic HBM bytes, callable)
+    stages = [
+        ("quantize_x_e4m3_tensor_t", 0, TOK * D * (2 + 2 + 1 + 1),
+         lambda: fm.quantize(x, fm.E4M3, fm.TENSOR, want_t=True, counters=ctr, scale=xs, out=xq, out_t=xqt)),
+        ("gemm_fwd_65536x3072x768", 2 * TOK * F * D, TOK * D + F * D + TOK * F * 2,
+         lambda: fm.scaled_mm(xq, fm.E4M3, xs, fm.TENSOR, cache.q, fm.E4M3, cache.scale, fm.TENSOR,
+                              out=y, counters=ctr)),
+        ("quantize_dy_e5m2_tensor_t", 0, TOK * F * (2 + 2 + 1 + 1),
+         lambda: fm.quantize(dy, fm.E5M2, fm.TENSOR, want_t=True, counters=ctr, scale=dys, out=dyq, out_t=dyqt)),
+        ("gemm_dx_65536x768x3072", 2 * TOK * D * F, TOK * F + D * F + TOK * D * 2,
+         lambda: fm.scaled_mm(dyq, fm.E5M2, dys, fm.TENSOR, cache.q_t, fm.E4M3, cache.scale, fm.TENSOR,
+                              out=dx, counters=ctr)),
+        ("gemm_dw_3072x768x65536", 2 * F * D * TOK, F * TOK + D * TOK + F * D * 2,
+         lambda: fm.scaled_mm(dyqt, fm.E5M2, dys, fm.TENSOR, xqt, fm.E4M3, xs, fm.TENSOR,
+                              out=dw, counters=ctr, workspace=dw_ws)),
+        ("requant_w_cache", 0, F * D * (2 + 2 + 1 + 1),
+         lambda: fm.requant_weights([cache], [w_master])),
+        ("quantize_a_1x128", 0, FA_M * FA_K * 3 + FA_M * (FA_K // 128) * 4,
+         lambda: fm.quantize(a_fine, fm.E4M3, fm.ROW_1x128, scale=sa, out=aq, counters=ctr)),
+        ("quantize_b_128x128", 0, FA_N * FA_K * 3 + (FA_N // 128) * (FA_K // 128) * 4,
+         lambda: fm.quantize(b_fine, fm.E4M3, fm.BLOCK_128x128, scale=sb, out=bq, counters=ctr)),
+        ("gemm_block_16384x2048x7168", 2 * FA_M * FA_N * FA_K, FA_M * FA_K + FA_N * FA_K + FA_M * FA_N * 2
+         + FA_M * (FA_K // 128) * 4,
+         lambda: fm.scaled_mm(aq, fm.E4M3, sa, fm.ROW_1x128, bq, fm.E4M3, sb, fm.BLOCK_128x128,
+                              out=yf, counters=ctr)),
+    ]
+    step_flops = sum(s[1] for s in stages)
+
+    def step(events=None):
+        # the optimizer's master update precedes the cache refresh (not timed
+        # as part of the FP8 path: it is the caller's optimizer)
+        for i, (_, _, _, fn) in enumerate(stages):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(ev[k])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    stage_ms = {}
+    for i, (name, flops, nbytes, _) in enumerate(stages):
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
+        stage_ms[name] = ms
+    kernels = {}
+    for name, flops, nbytes, _ in stages:
+        ms = stage_ms[name]
+        d = {"ms": round(ms, 4)}
+        if flops:
+            d["tflops"] = round(flops / ms / 1e9, 1)
+            d["frac_fp8_peak"] = round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4)
+        d["gbs"] = round(nbytes / ms / 1e6, 1)
+        d["frac_hbm"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)
+        kernels[name] = d
+
+    # dominant kernel: the single-kernel GEMM stage with the largest share
+    single_kernel_gemms = ["gemm_fwd_65536x3072x768", "gemm_dx_65536x768x3072", "gemm_block_16384x2048x7168"]
+    dom = max(single_kernel_gemms, key=lambda n: stage_ms[n])
+    dflops = [s[1] for s in stages if s[0] == dom][0]
+    achieved = dflops / stage_ms[dom] / 1e9
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None}
+
+    counters = ctr.read()
+    value = step_flops / (ms_per_step / 1e3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_sample_rows, stage_ms)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (e4m3/e5m2) x fp8 -> fp32 accumulate -> bf16",
+        "data": "synthetic (seeded; bf16 N(0,1)/N(0,0.02)/N(0,1e-3), 1% channels x100 for the block-scaled GEMM)",
+        "config": {
+            "workload": "FP8 MLP up-projection training step, 64 seqs x 1024 tokens, d_model 768 -> 3072 "
+                        "(forward, E5M2 backward dX/dW, weight-cache refresh) + block-scaled "
+                        "16384x2048x7168 GEMM with 1x128 / 128x128 scales",
+            "tokens": TOK, "d_model": D, "d_ff": F,
+            "block_scaled_mnk": [FA_M, FA_N, FA_K],
+            "step_gemm_gflop": round(step_flops / 1e9, 2),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "counters": counters,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(sample_rows: int, stage_ms: dict):
+    """The oracle, as it stands, on a bounded sample of the same work: a
+    row sample of the forward up-projection (quantize X rows with the oracle,
+    then its fp64 GEMM against all of W).  Reported in the metric's unit."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    x = synth.normal_bf16(3, 0, (TOK, D), 1.0)[:sample_rows]
+    w = synth.normal_bf16(3, 1, (F, D), 0.02)
+    t0 = time.time()
+    xq, _, xs, _ = oracle.quantize(x, oracle.E4M3)
+    wq, _, ws, _ = oracle.quantize(w, oracle.E4M3)
+    y = oracle.gemm(xq, 0, xs, 0, wq, 0, ws, 0)
+    dt = time.time() - t0
+    flops = 2.0 * sample_rows * F * D
+    del y
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"forward up-projection on {sample_rows} of {TOK} token rows: oracle quantize of X rows "
+                      f"and W, then fp64 GEMM {sample_rows}x{F}x{D}; {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+"""Python binding of the MI355X FP8 scaled-matmul library (libfp8mi.so).
+
+Argument marshalling only: every step of quantization, GEMM and cache refresh
+runs in the HIP kernels behind the C ABI declared in include/fp8mi.h.  Torch
+supplies device memory and the current stream; nothing here computes.
+
+The functions named ``fp8_*`` mirror the C entry points one to one (raw
+device pointers as ints).  The tensor-level helpers (``quantize``,
+``scaled_mm``, ``WeightCache`` ...) allocate outputs and workspaces with torch
+and call those.
+
+If the library has not been built, importing works but every call raises
+``RuntimeError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfp8mi.so")
+
+# enums of include/fp8mi.h
+FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_UNSUPPORTED_DEVICE, FP8_ERR_HIP = range(5)
+E4M3, E5M2 = 0, 1
+BF16, FP32 = 0, 1
+TENSOR, ROW_1x128, BLOCK_128x128 = 0, 1, 2
+FROM_AMAX, GIVEN = 0, 1
+
+EXPORTED = [
+    "fp8_abi_version", "fp8_status_string", "fp8_last_error",
+    "fp8_amax_workspace_size", "fp8_amax",
+    "fp8_quantize_workspace_size", "fp8_quantize",
+    "fp8_scaled_mm_workspace_size", "fp8_scaled_mm",
+    "fp8_requant_workspace_size", "fp8_requant_weights",
+    "fp8_counters_reset",
+]
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+class WeightCacheDesc(ctypes.Structure):
+    """fp8_weight_cache of include/fp8mi.h."""
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("fmt", ctypes.c_int), ("gran", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("q_t", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("ctr", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp8mi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fp8_scaled_matmul_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.fp8_abi_version.restype = ctypes.c_int32
+        L.fp8_abi_version.argtypes = []
+        L.fp8_status_string.restype = ctypes.c_char_p
+        L.fp8_status_string.argtypes = [i32]
+        L.fp8_last_error.restype = ctypes.c_char_p
+        L.fp8_last_error.argtypes = []
+        L.fp8_amax_workspace_size.restype = sz
+        L.fp8_amax_workspace_size.argtypes = [i64, i64, i32]
+        L.fp8_amax.restype = i32
+        L.fp8_amax.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, sz, vp]
+        L.fp8_quantize_workspace_size.restype = sz
+        L.fp8_quantize_workspace_size.argtypes = [i64, i64, i32, i32]
+        L.fp8_quantize.restype = i32
+        L.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, vp,
+                                   vp, i64, vp, i64, vp, vp, sz, vp]
+        L.fp8_scaled_mm_workspace_size.restype = sz
+        L.fp8_scaled_mm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+        L.fp8_scaled_mm.restype = i32
+        L.fp8_scaled_mm.argtypes = [vp, i32, i64, vp, i32, vp, i32, i64, vp, i32,
+                                    i64, i64, i64, vp, i64, vp, sz, vp, vp]
+        L.fp8_requant_workspace_size.restype = sz
+        L.fp8_requant_workspace_size.argtypes = [ctypes.POINTER(WeightCacheDesc), ctypes.c_int32]
+        L.fp8_requant_weights.restype = i32
+        L.fp8_requant_weights.argtypes = [ctypes.POINTER(WeightCacheDesc), ctypes.POINTER(vp),
+                                          ctypes.POINTER(ctypes.c_int), ctypes.c_int32, vp, sz, vp]
+        L.fp8_counters_reset.restype = i32
+        L.fp8_counters_reset.argtypes = [vp, vp]
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().fp8_status_string(s).decode()
+    except Exception:
+        return f"status {s}"
+
+
+def check(status: int) -> None:
+    if status != FP8_OK:
+        raise Fp8Error(status, lib().fp8_last_error().decode())
+
+
+# ---------------------------------------------------------------- raw C entry points
+def fp8_abi_version() -> int:
+    return lib().fp8_abi_version()
+
+
+def fp8_amax(x, dtype, rows, cols, ld, gran, amax, workspace, workspace_bytes, stream) -> int:
+    return lib().fp8_amax(x, dtype, rows, cols, ld, gran, amax, workspace, workspace_bytes, stream)
+
+
+def fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
+                 workspace, workspace_bytes, stream) -> int:
+    return lib().fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
+                              workspace, workspace_bytes, stream)
+
+
+def fp8_scaled_mm(a, fa, lda, scale_a, ga, b, fb, ldb, scale_b, gb, m, n, k, c, ldc,
+                  workspace, workspace_bytes, ctr, stream) -> int:
+    return lib().fp8_scaled_mm(a, fa, lda, scale_a, ga, b, fb, ldb, scale_b, gb, m, n, k, c, ldc,
+                               workspace, workspace_bytes, ctr, stream)
+
+
+def fp8_requant_weights(descs, masters, dtypes, workspace, workspace_bytes, stream) -> int:
+    n = len(descs)
+    arr = (WeightCacheDesc * n)(*descs)
+    mp = (ctypes.c_void_p * n)(*masters)
+    dt = (ctypes.c_int * n)(*dtypes)
+    return lib().fp8_requant_weights(arr, mp, dt, n, workspace, workspace_bytes, stream)
+
+
+def fp8_counters_reset(ctr, stream) -> int:
+    return lib().fp8_counters_reset(ctr, stream)
+
+
+# ---------------------------------------------------------------- torch-level helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError("inputs are bfloat16 or float32 tensors")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_2d(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+
+
+def scale_shape(gran: int, rows: int, cols: int) -> tuple[int, ...]:
+    nt = -(-cols // 128)
+    if gran == TENSOR:
+        return (1,)
+    if gran == ROW_1x128:
+        return (rows, nt)
+    return (-(-rows // 128), nt)
+
+
+class Counters:
+    """The 4 x uint64 telemetry block in device memory (saturated, underflow,
+    nan, nonfinite_out)."""
+    FIELDS = ("saturated", "underflow", "nan", "nonfinite_out")
+
+    def __init__(self, device="cuda"):
+        torch = _torch()
+        self.buf = torch.zeros(4, dtype=torch.int64, device=device)
+
+    def ptr(self):
+        return self.buf.data_ptr()
+
+    def reset(self):
+        check(fp8_counters_reset(self.ptr(), _stream()))
+
+    def read(self) -> dict:
+        vals = self.buf.cpu().tolist()
+        return {f: int(v) & 0xFFFFFFFFFFFFFFFF for f, v in zip(self.FIELDS, vals)}
+
+
+def amax(x, gran: int = TENSOR):
+    torch = _torch()
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    out = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
+    wsb = lib().fp8_amax_workspace_size(rows, cols, gran)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    check(fp8_amax(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), gran, out.data_ptr(),
+                   ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scale=None,
+             want_t: bool = False, counters: Counters | None = None, out=None, out_t=None):
+    """Returns (q uint8 [rows, cols], q_t uint8 [cols, rows] or None, scale fp32)."""
+    torch = _torch()
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    if scale is None:
+        if mode == GIVEN:
+            raise ValueError("GIVEN mode needs a scale tensor")
+        scale = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
+    q = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    qt = None
+    if want_t:
+        qt = out_t if out_t is not None else torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    wsb = lib().fp8_quantize_workspace_size(rows, cols, gran, mode)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    check(fp8_quantize(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), fmt, gran, mode,
+                       scale.data_ptr(), q.data_ptr(), q.stride(0),
+                       _ptr(qt), qt.stride(0) if qt is not None else 0,
+                       counters.ptr() if counters else None, ws.data_ptr(), wsb, _stream()))
+    return q, qt, scale
+
+
+def scaled_mm(a, fa: int, scale_a, ga: int, b, fb: int, scale_b, gb: int,
+              out=None, counters: Counters | None = None, workspace=None):
+    """y = (s_a A)(s_b B)^T, a [m,k] uint8, b [n,k] uint8 -> bf16 [m,n]."""
+    torch = _torch()
+    _check_2d(a, "a")
+    _check_2d(b, "b")
+    m, k = a.shape
+    n, k2 = b.shape
+    if k != k2:
+        raise ValueError("a and b disagree on k")
+    c = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    wsb = lib().fp8_scaled_mm_workspace_size(m, n, k, ga, gb)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    check(fp8_scaled_mm(a.data_ptr(), fa, a.stride(0), scale_a.data_ptr(), ga,
+                        b.data_ptr(), fb, b.stride(0), scale_b.data_ptr(), gb,
+                        m, n, k, c.data_ptr(), c.stride(0),
+                        _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                        counters.ptr() if counters else None, _stream()))
+    return c
+
+
+class WeightCache:
+    """FP8 compute copy of one master weight [rows, cols] ("#84 FP8
+    Precision", section "Hardware precision": re-quantized after each optimizer
+    step, read by the next forward).  q is the [N, K] operand of the forward
+    GEMM, q_t the K-contiguous operand of the backward dX GEMM."""
+
+    def __init__(self, rows: int, cols: int, fmt: int = E4M3, gran: int = TENSOR,
+                 with_t: bool = True, counters: Counters | None = None, device="cuda"):
+        torch = _torch()
+        self.rows, self.cols, self.fmt, self.gran = rows, cols, fmt, gran
+        self.q = torch.empty((rows, cols), dtype=torch.uint8, device=device)
+        self.q_t = torch.empty((cols, rows), dtype=torch.uint8, device=device) if with_t else None
+        self.scale = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=device)
+        self.counters = counters
+
+    def desc(self) -> WeightCacheDesc:
+        return WeightCacheDesc(self.rows, self.cols, self.fmt, self.gran, self.q.data_ptr(),
+                               _ptr(self.q_t), self.scale.data_ptr(),
+                               self.counters.ptr() if self.counters else None)
+
+
+def requant_weights(caches: list[WeightCache], masters: list) -> None:
+    """Refresh every cache from its master in one call."""
+    torch = _torch()
+    if not caches:
+        return
+    descs = [c.desc() for c in caches]
+    arr = (WeightCacheDesc * len(descs))(*descs)
+    wsb = lib().fp8_requant_workspace_size(arr, len(descs))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=masters[0].device)
+    for c, m in zip(caches, masters):
+        if tuple(m.shape) != (c.rows, c.cols) or not m.is_contiguous():
+            raise ValueError("master must be contiguous with the cache's shape")
+    check(fp8_requant_weights(descs, [m.data_ptr() for m in masters], [_dtype_code(m) for m in masters],
+                              ws.data_ptr(), wsb, _stream()))

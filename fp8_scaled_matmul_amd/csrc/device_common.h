@@ -1,0 +1,186 @@
+// Device-side helpers shared by the quantizer kernels: FP8 format traits, the
+// scaled quotient, the saturating cast to OCP E4M3 / E5M2 and counter
+// reduction.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8mi.h"
+
+namespace fp8mi {
+
+// OCP E4M3 (max 448) and E5M2 (max 57344): the maxima printed in "FP8
+// stability guardrails", section "Why FP8 is tempting and why it is fragile".
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> {
+    static constexpr float fmax = 448.0f;
+    static constexpr uint32_t maxcode = 0x7E;
+    // Round-to-nearest-even with no upper exponent bound sends |v| <= 464 to
+    // 448 (464 is the tie between 448 and 480, 448 has the even mantissa) and
+    // anything larger past the range: that is a saturation event.
+    __device__ static bool saturates(float a) { return a > 464.0f; }
+    // Largest |v| that rounds to zero: half the smallest subnormal 2^-9,
+    // which ties to the even code 0.
+    static constexpr float zero_below_eq = 0x1p-10f;
+};
+template <> struct Fmt<1> {
+    static constexpr float fmax = 57344.0f;
+    static constexpr uint32_t maxcode = 0x7B;
+    // 61440 ties 57344 (odd mantissa) and 65536 (even): rounds up, saturates.
+    __device__ static bool saturates(float a) { return a >= 61440.0f; }
+    static constexpr float zero_below_eq = 0x1p-17f;
+};
+
+// Scales at or above this use the multiply + correction quotient; smaller
+// ones take a full IEEE division (see quot_corrected).
+constexpr float kCorrectedQuotMinScale = 0x1p-64f;
+
+// Dequantization scale from an amax: s = fl32(amax / fmax), 1 for amax 0,
+// raised to FLT_MIN when smaller (so no result depends on denormal scales).
+template <int FMT>
+__device__ inline float scale_from_amax(float amax)
+{
+    if (amax == 0.0f) return 1.0f;
+    float s = amax / Fmt<FMT>::fmax;            // correctly rounded fp32 division
+    return s < 0x1p-126f ? 0x1p-126f : s;
+}
+
+// v = fl32(x / s) for |x| <= amax of the group and s >= 2^-64, from the
+// correctly rounded reciprocal r = fl32(1/s): q0 = x r, residual
+// e = x - q0 s (exact by FMA), v = q0 + e r (P. Markstein, "IA-64 and
+// Elementary Functions", 2000).  The copysign restores the sign of zero
+// quotients.  Checked exhaustively on the CPU over every finite bf16 x and
+// every scale a bf16 amax can produce: the FP8 code and counter events equal
+// those of the IEEE quotient in every case.
+__device__ inline float quot_corrected(float x, float s, float r)
+{
+    float q0 = x * r;
+    float e = __builtin_fmaf(-q0, s, x);
+    float v = __builtin_fmaf(e, r, q0);
+    return __builtin_copysignf(v, x);
+}
+
+// Two fp32 values (already clamped to +-fmax) to two FP8 bytes; hi selects
+// bytes 2-3 of `old`.  The hardware conversion rounds to nearest even.
+template <int FMT, bool HI>
+__device__ inline int cvt_pk(float a, float b, int old)
+{
+    if constexpr (FMT == 0)
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+    else
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+}
+
+template <int FMT>
+__device__ inline float clamp_fmax(float v)
+{
+    return __builtin_amdgcn_fmed3f(v, -Fmt<FMT>::fmax, Fmt<FMT>::fmax);
+}
+
+// Four quotients (finite, |v| bounded by about fmax) to four codes, plus the
+// count of underflows (non-zero x whose code is +-0).
+template <int FMT>
+__device__ inline uint32_t encode4_fast(const float v[4], const float x[4], uint32_t& und)
+{
+    int w = cvt_pk<FMT, false>(clamp_fmax<FMT>(v[0]), clamp_fmax<FMT>(v[1]), 0);
+    w = cvt_pk<FMT, true>(clamp_fmax<FMT>(v[2]), clamp_fmax<FMT>(v[3]), w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        und += (__builtin_fabsf(v[i]) <= Fmt<FMT>::zero_below_eq) & (x[i] != 0.0f);
+    return (uint32_t)w;
+}
+
+// General per-element encode for any quotient (NaN, Inf, out of range), with
+// all three counters.  NaN quotients get 0x7F with sign(x) xor sign(s).
+template <int FMT>
+__device__ inline uint32_t encode4_general(const float v[4], const float x[4], float s,
+                                           uint32_t& sat, uint32_t& und, uint32_t& nan)
+{
+    int w = cvt_pk<FMT, false>(clamp_fmax<FMT>(v[0]), clamp_fmax<FMT>(v[1]), 0);
+    w = cvt_pk<FMT, true>(clamp_fmax<FMT>(v[2]), clamp_fmax<FMT>(v[3]), w);
+    uint32_t out = (uint32_t)w;
+    const uint32_t ssign = __builtin_bit_cast(uint32_t, s) >> 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        if (v[i] != v[i]) {
+            const uint32_t sg = (__builtin_bit_cast(uint32_t, x[i]) >> 31) ^ ssign;
+            out = (out & ~(0xFFu << (8 * i))) | (((sg << 7) | 0x7Fu) << (8 * i));
+            nan += 1;
+        } else {
+            sat += Fmt<FMT>::saturates(a);
+            und += (a <= Fmt<FMT>::zero_below_eq) & (x[i] != 0.0f);
+        }
+    }
+    return out;
+}
+
+__device__ inline uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ inline uint32_t wave_max(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Adds per-thread counts to the device counters: one atomic per wave and
+// counter, skipped when the wave's count is zero.
+__device__ inline void flush_counters(fp8_counters* ctr, uint32_t sat, uint32_t und, uint32_t nan,
+                                      uint32_t nonfinite = 0)
+{
+    if (!ctr) return;
+    sat = wave_sum(sat);
+    und = wave_sum(und);
+    nan = wave_sum(nan);
+    nonfinite = wave_sum(nonfinite);
+    if ((threadIdx.x & 63) == 0) {
+        if (sat) atomicAdd((unsigned long long*)&ctr->saturated, (unsigned long long)sat);
+        if (und) atomicAdd((unsigned long long*)&ctr->underflow, (unsigned long long)und);
+        if (nan) atomicAdd((unsigned long long*)&ctr->nan, (unsigned long long)nan);
+        if (nonfinite) atomicAdd((unsigned long long*)&ctr->nonfinite_out, (unsigned long long)nonfinite);
+    }
+}
+
+// |x| as an ordered integer key for finite x, 0 for Inf/NaN (amax ignores
+// them); bit 31 flags a non-finite element.
+__device__ inline uint32_t absbits_bf16(uint32_t h)
+{
+    const uint32_t a = h & 0x7FFFu;
+    return a < 0x7F80u ? (a << 16) : 0x80000000u;
+}
+__device__ inline uint32_t absbits_f32(uint32_t w)
+{
+    const uint32_t a = w & 0x7FFFFFFFu;
+    return a < 0x7F800000u ? a : 0x80000000u;
+}
+// Combine two keys: max of the magnitudes, OR of the non-finite flags.
+__device__ inline uint32_t key_merge(uint32_t p, uint32_t q)
+{
+    const uint32_t m = max(p & 0x7FFFFFFFu, q & 0x7FFFFFFFu);
+    return m | ((p | q) & 0x80000000u);
+}
+__device__ inline float key_amax(uint32_t k) { return __builtin_bit_cast(float, k & 0x7FFFFFFFu); }
+__device__ inline bool key_special(uint32_t k) { return (k >> 31) != 0; }
+
+__device__ inline uint32_t wave_key_merge(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = key_merge(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Unpack bf16 pairs to fp32.
+__device__ inline float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+}  // namespace fp8mi

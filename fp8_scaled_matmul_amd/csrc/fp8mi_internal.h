@@ -1,0 +1,61 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernel files.
+// Not installed; the public interface is include/fp8mi.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fp8mi.h"
+
+namespace fp8mi {
+
+// Number of per-workgroup partial maxima the per-tensor amax pass writes.
+constexpr int kAmaxPartials = 1024;
+constexpr size_t kAmaxWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
+
+// Quantizer launch description (all pointers device pointers).
+struct QuantArgs {
+    const void* x;
+    int dtype;          // FP8_IN_BF16 / FP8_IN_FP32
+    int64_t rows, cols, ld;
+    int fmt;            // FP8_E4M3 / FP8_E5M2
+    int gran;           // FP8_TENSOR / FP8_ROW_1x128 / FP8_BLOCK_128x128
+    int mode;           // FP8_SCALE_FROM_AMAX / FP8_SCALE_GIVEN
+    float* scale;
+    uint8_t* q;
+    int64_t ldq;
+    uint8_t* qt;        // nullable
+    int64_t ldqt;
+    fp8_counters* ctr;  // nullable
+    uint32_t* partials; // per-tensor FROM_AMAX workspace
+};
+
+// Each launcher enqueues on `stream` and returns the hipError_t of the launch.
+hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                              float* out, uint32_t* partials, hipStream_t stream);
+hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                               int gran, float* out, hipStream_t stream);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_counters_reset(fp8_counters* ctr, hipStream_t stream);
+
+struct GemmArgs {
+    const uint8_t* a;
+    const uint8_t* b;
+    int64_t lda, ldb;
+    const float* sa;
+    const float* sb;
+    int fa, fb;
+    bool block_scaled;
+    int64_t m, n, k;
+    void* c;
+    int64_t ldc;
+    float* ws;          // split-K partials, or nullptr
+    int splits;
+    fp8_counters* ctr;
+};
+
+int gemm_choose_splits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace fp8mi

@@ -1,0 +1,367 @@
+// Scaled FP8 GEMM for gfx950: y = (s_a A_q)(s_b B_q)^T, A [m,k] and B [n,k]
+// both K-contiguous (the TN form _scaled_mm(x, w_fp8, scale_a, scale_b) takes,
+// "#84 FP8 Precision", code excerpt), fp32 accumulation on the CDNA4 FP8
+// matrix cores, bf16 output.  Block-scaled form: per 128-wide K block, the
+// partial product of each 16x16 output tile is promoted into the fp32
+// accumulator with s_a[row, kb] * s_b[n/128, kb] ("fine grained tile and block
+// scaling", "FP8 stability guardrails", section "Real products").
+//
+// Design (one workgroup per 256x256 output tile, 4 waves of 128x128):
+//   - K steps of 128 bytes; A and B tiles staged in LDS (2 x 64 KB, double
+//     buffered) with a 16-byte-chunk XOR swizzle that keeps both the row-wise
+//     fills and the fragment reads free of bank conflicts;
+//   - v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales (exponent 127):
+//     every instruction covers exactly one 128-wide K block;
+//   - workgroup ids are spread over the 8 XCDs so that each XCD walks a
+//     contiguous, M-grouped range of output tiles (A panels stay in its L2);
+//   - optional split over K with fp32 partials reduced in a fixed order.
+#include <hip/hip_bf16.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "fp8mi_internal.h"
+
+namespace fp8mi {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kGemmThreads = 256;
+constexpr int kGroupM = 8;
+constexpr int kTileBytes = BM * BK;       // 32 KB per operand tile
+
+// 16-byte chunk c (0..7) of row r lives at chunk position swz(r, c).  Any 8
+// consecutive rows reading the same logical chunk land in 8 distinct
+// positions, and any 16 consecutive rows cover all 16 (row parity x
+// position) slots of a 256-byte bank line.
+__device__ inline int swz(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
+
+template <int FA, int FB>
+__device__ inline v4f mfma(const v8i& a, const v8i& b, const v4f& c)
+{
+    // unit block scales: E8M0 exponent 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+}
+
+struct KArgs {
+    const uint8_t* a;
+    const uint8_t* b;
+    int64_t lda, ldb;
+    const float* sa;
+    const float* sb;
+    int m, n, k;
+    uint16_t* c;
+    int64_t ldc;
+    float* ws;
+    int splits;
+    int ktiles;          // ceil(k / BK)
+    int tiles_m, tiles_n;
+    fp8_counters* ctr;
+};
+
+// Global -> register staging of one 256x128 operand tile: thread t loads
+// chunks (row t/8 + 32 i, chunk t%8), i = 0..7; rows past `rows` and K past
+// `k` read as zero.
+__device__ inline void load_tile(const uint8_t* base, int64_t ld, int row0, int rows, int k0, int k,
+                                 uint4 regs[8])
+{
+    const int t = threadIdx.x;
+    const int c = t & 7;
+    const int kk = k0 + c * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (t >> 3) + 32 * i;
+        if (row0 + r < rows && kk < k)
+            regs[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(row0 + r) * ld + kk);
+        else
+            regs[i] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+__device__ inline void store_tile(uint8_t* lds, const uint4 regs[8])
+{
+    const int t = threadIdx.x;
+    const int c = t & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (t >> 3) + 32 * i;
+        *reinterpret_cast<uint4*>(lds + r * BK + swz(r, c) * 16) = regs[i];
+    }
+}
+
+// MFMA operand fragment for rows row0..row0+15 of a staged tile: lane l holds
+// row row0 + l%16, K bytes 32*(l/16) .. +32 (the same K assignment is used for
+// A and B, so the products pair up element for element).
+__device__ inline v8i load_frag(const uint8_t* lds, int row0)
+{
+    const int l = threadIdx.x & 63;
+    const int r = row0 + (l & 15);
+    const int c0 = (l >> 4) * 2;
+    const uint4 lo = *reinterpret_cast<const uint4*>(lds + r * BK + swz(r, c0) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(lds + r * BK + swz(r, c0 + 1) * 16);
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+}
+
+__device__ inline uint16_t to_bf16(float v)
+{
+    return __builtin_bit_cast(uint16_t, __float2bfloat16(v));
+}
+
+// Map a linear workgroup id to (split, tile_m, tile_n).  Hardware hands ids
+// to XCDs round robin; re-number so that XCD x owns a contiguous block of
+// logical ids, then walk tiles M-grouped (kGroupM tile rows at a time).
+__device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn)
+{
+    const int total = p.tiles_m * p.tiles_n * p.splits;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, local = bid >> 3;
+    const int q = total >> 3, rem = total & 7;
+    const int pid = xcd * q + min(xcd, rem) + local;
+    const int per_split = p.tiles_m * p.tiles_n;
+    split = pid / per_split;
+    const int t = pid - split * per_split;
+    const int in_group = kGroupM * p.tiles_n;
+    const int g = t / in_group;
+    const int first_m = g * kGroupM;
+    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int r = t - g * in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+template <int FA, int FB, bool BLOCK>
+__global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTileBytes];
+    __shared__ float lds_sa[2][BM];
+
+    int split, tm, tn;
+    tile_of(p, split, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kt_per = (p.ktiles + p.splits - 1) / p.splits;
+    const int kt0 = split * kt_per;
+    const int kt1 = min(p.ktiles, kt0 + kt_per);
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wm = (wave >> 1) * 128;
+    const int wn = (wave & 1) * 128;
+    const int nkb = p.k / BK;   // block-scale columns (k % 128 == 0 in block mode)
+
+    v4f acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint4 ra[8], rb[8];
+    float rsa = 0.0f;
+    if (kt0 < kt1) {
+        load_tile(p.a, p.lda, m0, p.m, kt0 * BK, p.k, ra);
+        load_tile(p.b, p.ldb, n0, p.n, kt0 * BK, p.k, rb);
+        if constexpr (BLOCK)
+            rsa = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt0] : 0.0f;
+        store_tile(lds_a[0], ra);
+        store_tile(lds_b[0], rb);
+        if constexpr (BLOCK) lds_sa[0][threadIdx.x] = rsa;
+    }
+    __syncthreads();
+
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        const bool more = kt + 1 < kt1;
+        if (more) {
+            load_tile(p.a, p.lda, m0, p.m, (kt + 1) * BK, p.k, ra);
+            load_tile(p.b, p.ldb, n0, p.n, (kt + 1) * BK, p.k, rb);
+            if constexpr (BLOCK)
+                rsa = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt + 1] : 0.0f;
+        }
+        const uint8_t* la = lds_a[buf];
+        const uint8_t* lb = lds_b[buf];
+        v8i bf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bf[j] = load_frag(lb, wn + 16 * j);
+        if constexpr (!BLOCK) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const v8i af = load_frag(la, wm + 16 * i);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af, bf[j], acc[i][j]);
+            }
+        } else {
+            // s_b of this wave's 128 columns and this K block (uniform)
+            const int nb = (n0 + wn) / 128;
+            const float sbv = (n0 + wn < p.n) ? p.sb[(int64_t)nb * nkb + kt] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const v8i af = load_frag(la, wm + 16 * i);
+                const float4 sa4 = *reinterpret_cast<const float4*>(&lds_sa[buf][wm + 16 * i + 4 * (lane >> 4)]);
+                const float c0 = sa4.x * sbv, c1 = sa4.y * sbv, c2 = sa4.z * sbv, c3 = sa4.w * sbv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const v4f part = mfma<FA, FB>(af, bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                    acc[i][j][0] = __builtin_fmaf(part[0], c0, acc[i][j][0]);
+                    acc[i][j][1] = __builtin_fmaf(part[1], c1, acc[i][j][1]);
+                    acc[i][j][2] = __builtin_fmaf(part[2], c2, acc[i][j][2]);
+                    acc[i][j][3] = __builtin_fmaf(part[3], c3, acc[i][j][3]);
+                }
+            }
+        }
+        if (more) {
+            store_tile(lds_a[buf ^ 1], ra);
+            store_tile(lds_b[buf ^ 1], rb);
+            if constexpr (BLOCK) lds_sa[buf ^ 1][threadIdx.x] = rsa;
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column n0+wn+16j+lane%16, rows m0+wm+16i+4(lane/16)+r
+    const int col_l = lane & 15;
+    const int row_l = 4 * (lane >> 4);
+    if (p.ws) {
+        float* ws = p.ws + (int64_t)split * p.m * p.n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = n0 + wn + 16 * j + col_l;
+                if (col >= p.n) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm + 16 * i + row_l + r;
+                    if (row < p.m) ws[(int64_t)row * p.n + col] = acc[i][j][r];
+                }
+            }
+        return;
+    }
+    const float scale = BLOCK ? 1.0f : p.sa[0] * p.sb[0];
+    uint32_t nonfinite = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = n0 + wn + 16 * j + col_l;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm + 16 * i + row_l + r;
+                if (row < p.m && col < p.n) {
+                    const uint16_t h = to_bf16(acc[i][j][r] * scale);
+                    nonfinite += (h & 0x7F80u) == 0x7F80u;
+                    p.c[(int64_t)row * p.ldc + col] = h;
+                }
+            }
+        }
+    flush_counters(p.ctr, 0, 0, 0, nonfinite);
+}
+
+// Fixed-order reduction of split-K partials: y = bf16(scale * sum_s ws[s]).
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float* ws, int splits, int m, int n, float scale_mode_tensor,
+                                                       const float* sa, const float* sb, uint16_t* c, int64_t ldc,
+                                                       fp8_counters* ctr)
+{
+    const float scale = scale_mode_tensor != 0.0f ? sa[0] * sb[0] : 1.0f;
+    const int64_t total = (int64_t)m * n;
+    uint32_t nonfinite = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        float s = 0.0f;
+        for (int sp = 0; sp < splits; ++sp) s += ws[(int64_t)sp * total + i];
+        const uint16_t h = to_bf16(s * scale);
+        nonfinite += (h & 0x7F80u) == 0x7F80u;
+        const int64_t row = i / n, col = i - row * n;
+        c[row * ldc + col] = h;
+    }
+    flush_counters(ctr, 0, 0, 0, nonfinite);
+}
+
+__global__ void k_zero_bf16(uint16_t* c, int m, int n, int64_t ldc)
+{
+    const int64_t total = (int64_t)m * n;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / n, col = i - row * n;
+        c[row * ldc + col] = 0;
+    }
+}
+
+template <int FA, int FB>
+hipError_t gemm_fmt(const KArgs& p, bool block, int grid, hipStream_t stream)
+{
+    if (block)
+        hipLaunchKernelGGL((k_gemm<FA, FB, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_gemm<FA, FB, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Split K when the output has too few 256x256 tiles to fill the 256 CUs and
+// each split keeps at least 8 K steps.
+int gemm_choose_splits(int64_t m, int64_t n, int64_t k)
+{
+    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int64_t ktiles = (k + BK - 1) / BK;
+    if (tiles >= 128 || ktiles < 16) return 1;
+    int64_t s = 256 / tiles;                 // one wave of workgroups
+    s = std::min<int64_t>(s, ktiles / 8);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
+{
+    if (g.m == 0 || g.n == 0) return hipSuccess;
+    if (g.k == 0) {
+        const int64_t total = g.m * g.n;
+        const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
+        hipLaunchKernelGGL(k_zero_bf16, dim3(grid), dim3(256), 0, stream, static_cast<uint16_t*>(g.c), (int)g.m,
+                           (int)g.n, g.ldc);
+        return hipGetLastError();
+    }
+    KArgs p;
+    p.a = g.a;
+    p.b = g.b;
+    p.lda = g.lda;
+    p.ldb = g.ldb;
+    p.sa = g.sa;
+    p.sb = g.sb;
+    p.m = (int)g.m;
+    p.n = (int)g.n;
+    p.k = (int)g.k;
+    p.c = static_cast<uint16_t*>(g.c);
+    p.ldc = g.ldc;
+    p.ws = g.splits > 1 ? g.ws : nullptr;
+    p.splits = g.splits > 1 ? g.splits : 1;
+    p.ktiles = (int)((g.k + BK - 1) / BK);
+    p.tiles_m = (int)((g.m + BM - 1) / BM);
+    p.tiles_n = (int)((g.n + BN - 1) / BN);
+    p.ctr = g.ctr;
+    // never leave a split without K steps
+    if (p.splits > 1) {
+        const int kt_per = (p.ktiles + p.splits - 1) / p.splits;
+        p.splits = (p.ktiles + kt_per - 1) / kt_per;
+        if (p.splits == 1) p.ws = nullptr;
+    }
+    const int grid = p.tiles_m * p.tiles_n * p.splits;
+    hipError_t e;
+    if (g.fa == FP8_E4M3)
+        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, g.block_scaled, grid, stream)
+                             : gemm_fmt<0, 1>(p, g.block_scaled, grid, stream);
+    else
+        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, g.block_scaled, grid, stream)
+                             : gemm_fmt<1, 1>(p, g.block_scaled, grid, stream);
+    if (e != hipSuccess || !p.ws) return e;
+    const int64_t total = g.m * g.n;
+    const int rgrid = (int)std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(rgrid), dim3(256), 0, stream, p.ws, p.splits, p.m, p.n,
+                       g.block_scaled ? 0.0f : 1.0f, g.sa, g.sb, p.c, g.ldc, g.ctr);
+    return hipGetLastError();
+}
+
+}  // namespace fp8mi

@@ -1,0 +1,205 @@
+/*
+ * fp8mi.h -- C ABI of the MI355X (gfx950) FP8 scaled-matmul library.
+ *
+ * Three operations, as the pages describe them:
+ *   1. amax and a saturating round-to-nearest-even cast of bf16 (or fp32)
+ *      tensors to FP8 E4M3 (max 448) or E5M2 (max 57344), with one scale per
+ *      tensor, per 1x128 row tile or per 128x128 block;
+ *   2. the scaled GEMM y = (s_a A_q)(s_b B_q)^T, fp32 accumulation, bf16 out;
+ *   3. the FP8 weight-copy cache, re-quantized from the master weights after
+ *      every optimizer step.
+ *
+ * Conventions for every entry point:
+ *   - All tensor, scale, counter and workspace pointers are DEVICE pointers
+ *     owned by the caller.  The library never allocates device memory, never
+ *     frees caller memory and keeps no mutable global state (apart from the
+ *     per-device architecture probe and the thread-local error text).
+ *   - Every call only enqueues work on `stream` (NULL = the default stream)
+ *     and returns; it never synchronizes the host.  Scales computed on the
+ *     device stay on the device.
+ *   - Arguments are checked on the host BEFORE anything is enqueued; a call
+ *     that returns an error has enqueued nothing.  Device-side values (scales
+ *     given by the caller) are not inspected on the host.
+ *   - Row-major throughout.  "ld" arguments are leading dimensions in
+ *     elements of the tensor they belong to.
+ *   - Nothing throws or aborts across the ABI.  FP8_ERR_HIP carries detail in
+ *     fp8_last_error() (thread-local).
+ *   - Only gfx950 devices are accepted: any other device returns
+ *     FP8_ERR_UNSUPPORTED_DEVICE and nothing falls back to another path.
+ *
+ * FP8 encodings are the OCP ones (E4M3FN: bias 7, no Inf, S.1111.111 = NaN;
+ * E5M2: bias 15, IEEE-style Inf/NaN); these are the formats whose maxima are
+ * 448 and 57344 ("FP8 stability guardrails", section "Why FP8 is tempting and
+ * why it is fragile"; bit splits in "How to Enable FP8 Training in NanoChat",
+ * section "FP8 Training Modes Explained").
+ */
+#ifndef FP8MI_H
+#define FP8MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle, declared here so that this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
+#define FP8MI_ABI_VERSION 1
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad ld, bad enum, bad alignment */
+    FP8_ERR_UNSUPPORTED_SHAPE = 2,  /* a shape / granularity combination the operation does not take */
+    FP8_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
+    FP8_ERR_HIP = 4                 /* a HIP runtime call or launch failed; see fp8_last_error() */
+} fp8_status;
+
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
+typedef enum { FP8_IN_BF16 = 0, FP8_IN_FP32 = 1 } fp8_dtype;
+typedef enum { FP8_TENSOR = 0, FP8_ROW_1x128 = 1, FP8_BLOCK_128x128 = 2 } fp8_granularity;
+typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
+
+/* Telemetry ("summary statistics of clipping and overflow events", NanoChat
+ * FAQ; "overflow telemetry", guardrails explainer).  Lives in device memory;
+ * every call that takes a non-NULL pointer ADDS its events with integer
+ * atomics.  Reset with fp8_counters_reset().
+ *   saturated     - elements whose value x/s, rounded to nearest-even on the
+ *                   format's grid with no upper exponent bound, exceeds the
+ *                   format maximum (written as +-max), plus +-Inf inputs;
+ *   underflow     - non-zero inputs whose code is +-0 (sign kept);
+ *   nan           - NaN inputs (written as 0x7F | sign);
+ *   nonfinite_out - GEMM outputs that are +-Inf or NaN in bf16. */
+typedef struct {
+    uint64_t saturated;
+    uint64_t underflow;
+    uint64_t nan;
+    uint64_t nonfinite_out;
+} fp8_counters;
+
+int32_t     fp8_abi_version(void);
+const char* fp8_status_string(fp8_status s);
+const char* fp8_last_error(void);
+
+/* ------------------------------------------------------------------ amax
+ * max |x| over the finite elements of each scaling group ("measure each batch
+ * ... pick padding", guardrails explainer; amax history, "Real products").
+ *   x      [rows, cols], leading dimension ld >= cols, bf16 or fp32.
+ *   amax   out: 1 float (TENSOR), [rows, ceil(cols/128)] (ROW_1x128) or
+ *          [ceil(rows/128), ceil(cols/128)] (BLOCK_128x128), row-major.
+ *          A group with no finite element gets 0.
+ *   workspace  TENSOR needs fp8_amax_workspace_size() bytes (partial maxima);
+ *          other granularities need none (may be NULL).
+ * Sizes of zero are allowed (TENSOR writes 0). */
+size_t     fp8_amax_workspace_size(int64_t rows, int64_t cols, fp8_granularity gran);
+fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                    fp8_granularity gran, float* amax,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ quantize
+ * Scale, then cast: for each element of each scaling group
+ *     v = fl32(x / s)                    (IEEE fp32 division, exactly rounded)
+ *     q = round-to-nearest-even(v) on the format's grid, saturated to +-max
+ * ("Weights are divided by a learned scale before quantizing", #84 lab card,
+ * section "Explanation"; overflow saturates / tiny values underflow to zero,
+ * guardrails explainer).  NaN -> 0x7F|sign, +-Inf -> +-max.
+ *   mode FROM_AMAX: s = fl32(amax / fmax) per group (fmax 448 or 57344);
+ *       amax == 0 gives s = 1; s below FLT_MIN is raised to FLT_MIN.  The
+ *       scales are WRITTEN to `scale`.
+ *   mode GIVEN: the caller's scales are READ from `scale` (a "learned" or
+ *       fixed scale, #84 lab card, "Hardware precision") and used as they
+ *       are; they should be finite and > 0.
+ *   scale  1 float / [rows, ceil(cols/128)] / [ceil(rows/128), ceil(cols/128)]
+ *          row-major, as for fp8_amax.  These are DEQUANTIZATION multipliers
+ *          (x ~ s * decode(q)), the scale_a / scale_b of the scaled GEMM.
+ *   q      out [rows, cols] bytes, leading dimension ldq >= cols.
+ *   q_t    optional out (NULL = none): the byte transpose [cols, rows],
+ *          leading dimension ldq_t >= rows.  TENSOR and BLOCK_128x128 only
+ *          (a 1x128 row tile does not transpose into a 1x128 row tile:
+ *          FP8_ERR_UNSUPPORTED_SHAPE).
+ *   ctr    optional counters (NULL = none).
+ *   workspace  TENSOR + FROM_AMAX needs fp8_quantize_workspace_size() bytes;
+ *          the other modes need none.
+ * Alignment: x, q, q_t any; fast vector paths are taken when rows start on
+ * 16-byte boundaries. */
+size_t     fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity gran,
+                                       fp8_scale_mode mode);
+fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                        fp8_format fmt, fp8_granularity gran, fp8_scale_mode mode,
+                        float* scale,
+                        uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                        fp8_counters* ctr,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ scaled GEMM
+ * y = (s_a A_q)(s_b B_q)^T in the TN layout that _scaled_mm(x, w_fp8,
+ * scale_a, scale_b) implies (#84 lab card, code excerpt and "Explanation":
+ * the weight operand is K-contiguous):
+ *   a  [m, k] FP8 bytes, lda >= k;  b  [n, k] FP8 bytes, ldb >= k;
+ *   c  [m, n] bf16 out, ldc >= n.   fa, fb: any of E4M3 / E5M2.
+ * Scale pairs:
+ *   (TENSOR, TENSOR)            y = bf16(s_a[0] s_b[0] sum_k A B)
+ *   (ROW_1x128, BLOCK_128x128)  y = bf16(sum_kb s_a[m, kb] s_b[n/128, kb] sum_{k in kb} A B)
+ *       ("fine grained tile and block scaling", guardrails explainer,
+ *       "Real products"); s_a is [m, k/128], s_b is [ceil(n/128), k/128],
+ *       row-major; needs k % 128 == 0.
+ * Products are accumulated in fp32 by the MFMA units; the epilogue rounds to
+ * bf16 (nearest even).  Any other pair: FP8_ERR_UNSUPPORTED_SHAPE.
+ * Shape rules: k % 16 == 0, lda % 16 == 0, ldb % 16 == 0, a and b 16-byte
+ * aligned (else FP8_ERR_UNSUPPORTED_SHAPE); m, n any >= 0; k == 0 writes zeros.
+ * workspace: when fp8_scaled_mm_workspace_size() > 0 the call may split the K
+ * dimension into slices reduced in a fixed order (deterministic); a smaller
+ * workspace (or NULL) runs without the split (same result to tolerance,
+ * different rounding order).
+ * ctr: nonfinite_out counts outputs that are Inf/NaN in bf16. */
+size_t     fp8_scaled_mm_workspace_size(int64_t m, int64_t n, int64_t k,
+                                        fp8_granularity ga, fp8_granularity gb);
+fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda,
+                         const float* scale_a, fp8_granularity ga,
+                         const uint8_t* b, fp8_format fb, int64_t ldb,
+                         const float* scale_b, fp8_granularity gb,
+                         int64_t m, int64_t n, int64_t k,
+                         void* c_bf16, int64_t ldc,
+                         void* workspace, size_t workspace_bytes,
+                         fp8_counters* ctr, hipStream_t stream);
+
+/* ------------------------------------------------------------------ weight cache
+ * The FP8 compute copy of master weights: "After each optimizer step, the
+ * BF16 weights are re-quantized to FP8 and cached for the next forward pass"
+ * (#84 lab card, "Hardware precision"; quantize_weights_fp8 in its second
+ * code excerpt).  Each descriptor names caller-owned device storage:
+ *   rows, cols  shape of the master [rows, cols] (contiguous, ld = cols);
+ *   fmt, gran   format and granularity (TENSOR or BLOCK_128x128 here);
+ *   q           [rows, cols] bytes; q_t optional [cols, rows] bytes (the
+ *               K-contiguous operand for the transposed GEMM);
+ *   scale       1 float (TENSOR) or the block grid (BLOCK_128x128);
+ *   ctr         optional counters.
+ * fp8_requant_weights() re-quantizes every cache from its master with a
+ * fresh amax scale (current scaling), in two launches for all TENSOR caches
+ * (one amax pass, one cast pass) and one for all BLOCK caches.  The result is
+ * byte-identical to fp8_quantize(master, FROM_AMAX) of each.  masters[i] is a
+ * device pointer, master_dtypes[i] its dtype; the three arrays are HOST arrays
+ * of length count.  Workspace: fp8_requant_workspace_size(). */
+typedef struct {
+    int64_t rows, cols;
+    fp8_format fmt;
+    fp8_granularity gran;
+    uint8_t* q;
+    uint8_t* q_t;
+    float* scale;
+    fp8_counters* ctr;
+} fp8_weight_cache;
+
+size_t     fp8_requant_workspace_size(const fp8_weight_cache* caches, int32_t count);
+fp8_status fp8_requant_weights(const fp8_weight_cache* caches, const void* const* masters,
+                               const fp8_dtype* master_dtypes, int32_t count,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Zero a counter block on `stream` (a small fill kernel, safe to capture). */
+fp8_status fp8_counters_reset(fp8_counters* ctr, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,192 @@
+"""GPU parity of the scaled GEMM against the fp64 oracle, to the tolerance
+max|y - y_ref| <= 1e-2 max|y_ref| and relative Frobenius <= 5e-3: small and
+ragged shapes in full, every format pair, both scale pairs, split K, and the
+full-size up-projection / fine-grained / backward workloads on sampled
+outputs plus whole rows and columns."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_matmul_amd as fm
+import oracle
+import synth
+from gpu_util import assert_gemm_close, dev_bf16, dev_f32, dev_u8, host
+
+pytestmark = pytest.mark.gpu
+PAIRS = [(fm.E4M3, fm.E4M3), (fm.E5M2, fm.E4M3), (fm.E4M3, fm.E5M2), (fm.E5M2, fm.E5M2)]
+
+
+def _codes(fmt, g, shape, sigma=1.0):
+    """Codes of N(0, sigma) values quantized by the oracle (finite, realistic)."""
+    v = synth.f32_to_bf16_bits((g.standard_normal(shape) * sigma).astype(np.float32))
+    q, _, s, _ = oracle.quantize(v, fmt)
+    return q, s
+
+
+def _run(a, fa, sa, ga, b, fb, sb, gb, workspace=True, ctr=None):
+    A, B = dev_u8(a), dev_u8(b)
+    SA, SB = dev_f32(np.asarray(sa, np.float32).reshape(-1)), dev_f32(np.asarray(sb, np.float32).reshape(-1))
+    m, k = a.shape
+    n = b.shape[0]
+    ws = None
+    if not workspace:
+        ws = torch.empty(0, dtype=torch.uint8, device="cuda")
+    y = fm.scaled_mm(A, fa, SA, ga, B, fb, SB, gb, counters=ctr, workspace=ws if not workspace else None)
+    return host(y)
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (16, 16, 128), (33, 17, 256), (256, 256, 128),
+                                   (300, 280, 384), (257, 513, 784), (512, 256, 1024), (64, 1000, 48)])
+def test_tensor_scaled_small(fa, fb, m, n, k):
+    g = np.random.default_rng(m * 7 + n * 3 + k)
+    a, sa = _codes(fa, g, (m, k))
+    b, sb = _codes(fb, g, (n, k), 0.02)
+    y = _run(a, fa, sa, 0, b, fb, sb, 0)
+    ref = oracle.gemm(a, fa, sa, 0, b, fb, sb, 0)
+    assert_gemm_close(y, ref, f"{m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS[:2])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 512), (300, 384, 640), (17, 130, 128), (512, 512, 1024)])
+def test_block_scaled_small(fa, fb, m, n, k):
+    g = np.random.default_rng(m + n + k)
+    av = synth.channel_scaled_bf16(200, 0, 3, (m, k))
+    bv = synth.channel_scaled_bf16(200, 1, 4, (n, k))
+    a, _, sa, _ = oracle.quantize(av, fa, oracle.ROW_1x128)
+    b, _, sb, _ = oracle.quantize(bv, fb, oracle.BLOCK_128x128)
+    y = _run(a, fa, sa, 1, b, fb, sb, 2)
+    ref = oracle.gemm(a, fa, sa, 1, b, fb, sb, 2)
+    assert_gemm_close(y, ref, f"block {m}x{n}x{k}")
+    del g
+
+
+def test_split_k_and_determinism():
+    g = np.random.default_rng(9)
+    m, n, k = 512, 256, 8192
+    a, sa = _codes(fm.E5M2, g, (m, k), 1e-3)
+    b, sb = _codes(fm.E4M3, g, (n, k))
+    ref = oracle.gemm(a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0)
+    assert fm.lib().fp8_scaled_mm_workspace_size(m, n, k, 0, 0) > 0
+    y1 = _run(a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0)
+    y2 = _run(a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0)
+    assert np.array_equal(y1, y2), "split-K result not deterministic"
+    assert_gemm_close(y1, ref, "split-K")
+    y3 = _run(a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0, workspace=False)
+    assert_gemm_close(y3, ref, "no workspace")
+    # block-scaled with split K
+    av = synth.channel_scaled_bf16(201, 0, 3, (m, k))
+    bv = synth.channel_scaled_bf16(201, 1, 4, (n, k))
+    a, _, sa, _ = oracle.quantize(av, fm.E4M3, oracle.ROW_1x128)
+    b, _, sb, _ = oracle.quantize(bv, fm.E4M3, oracle.BLOCK_128x128)
+    y = _run(a, 0, sa, 1, b, 0, sb, 2)
+    assert_gemm_close(y, oracle.gemm(a, 0, sa, 1, b, 0, sb, 2), "block split-K")
+
+
+def test_k_zero_and_empty():
+    A = torch.zeros((8, 0), dtype=torch.uint8, device="cuda")
+    B = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    y = torch.full((8, 5), 7.0, dtype=torch.bfloat16, device="cuda")
+    fm.scaled_mm(A, 0, one, 0, B, 0, one, 0, out=y)
+    assert torch.all(y == 0)
+    A = torch.zeros((0, 32), dtype=torch.uint8, device="cuda")
+    B = torch.zeros((5, 32), dtype=torch.uint8, device="cuda")
+    y = fm.scaled_mm(A, 0, one, 0, B, 0, one, 0)
+    assert y.shape == (0, 5)
+
+
+def test_strided_operands_and_output():
+    g = np.random.default_rng(10)
+    m, n, k = 100, 70, 256
+    a, sa = _codes(0, g, (m, k + 64))
+    b, sb = _codes(0, g, (n, k + 32))
+    A, B = dev_u8(a)[:, :k], dev_u8(b)[:, 16:16 + k]
+    out = torch.full((m, n + 10), 1.0, dtype=torch.bfloat16, device="cuda")
+    fm.scaled_mm(A, 0, dev_f32(sa), 0, B, 0, dev_f32(sb), 0, out=out[:, :n])
+    y = host(out)
+    ref = oracle.gemm(np.ascontiguousarray(a[:, :k]), 0, sa, 0, np.ascontiguousarray(b[:, 16:16 + k]), 0, sb, 0)
+    assert_gemm_close(y[:, :n], ref, "strided")
+    assert np.all(y[:, n:] == 0x3F80), "wrote past n"
+
+
+def test_nonfinite_output_counter():
+    a = np.full((32, 128), 0x7E, np.uint8)          # 448
+    b = np.full((32, 128), 0x7E, np.uint8)
+    ctr = fm.Counters()
+    y = _run(a, 0, [1e30], 0, b, 0, [1e3], 0, ctr=ctr)
+    assert ctr.read()["nonfinite_out"] == 32 * 32
+    assert np.all((y & 0x7FFF) == 0x7F80)
+
+
+def _sample_points(m, n, g, count=3000):
+    pm = np.concatenate([g.integers(0, m, count), np.full(n, m - 1), np.arange(min(m, 512))])
+    pn = np.concatenate([g.integers(0, n, count), np.arange(n), np.full(min(m, 512), n - 1)])
+    return pm, pn
+
+
+def _check_points(y, a, fa, sa, ga, b, fb, sb, gb, g, what):
+    m, n = y.shape
+    pm, pn = _sample_points(m, n, g)
+    ref = oracle.gemm_points(a, fa, sa, ga, b, fb, sb, gb, pm, pn)
+    return assert_gemm_close(y[pm, pn], ref, what)
+
+
+def test_small_up_projection_workload_full():
+    """X [256,768] ~N(0,1), W [3072,768] ~N(0,0.02), per-tensor E4M3 amax
+    scales, quantized on the GPU; full output compared."""
+    x = synth.normal_bf16(1, 0, synth.SMALL_UP_PROJ["x"], 1.0)
+    w = synth.normal_bf16(1, 1, synth.SMALL_UP_PROJ["w"], 0.02)
+    xq, _, xs = fm.quantize(dev_bf16(x), fm.E4M3)
+    wq, _, ws = fm.quantize(dev_bf16(w), fm.E4M3)
+    y = host(fm.scaled_mm(xq, 0, xs, 0, wq, 0, ws, 0))
+    oxq, _, oxs, _ = oracle.quantize(x, 0)
+    owq, _, ows, _ = oracle.quantize(w, 0)
+    assert np.array_equal(host(xq), oxq) and np.array_equal(host(wq), owq)
+    assert_gemm_close(y, oracle.gemm(oxq, 0, oxs, 0, owq, 0, ows, 0), "up-proj 256")
+
+
+def test_speedrun_up_projection_workload_sampled():
+    x = synth.normal_bf16(3, 0, synth.SPEEDRUN_UP_PROJ["x"], 1.0)
+    w = synth.normal_bf16(3, 1, synth.SPEEDRUN_UP_PROJ["w"], 0.02)
+    xq, _, xs = fm.quantize(dev_bf16(x), fm.E4M3)
+    wq, _, ws = fm.quantize(dev_bf16(w), fm.E4M3)
+    ctr = fm.Counters()
+    y = host(fm.scaled_mm(xq, 0, xs, 0, wq, 0, ws, 0, counters=ctr))
+    assert ctr.read()["nonfinite_out"] == 0
+    g = np.random.default_rng(3)
+    _check_points(y, host(xq), 0, host(xs), 0, host(wq), 0, host(ws), 0, g, "up-proj 65536")
+
+
+def test_block_scaled_workload_sampled():
+    a = synth.channel_scaled_bf16(4, 0, 3, synth.BLOCK_SCALED["a"])
+    b = synth.channel_scaled_bf16(4, 1, 4, synth.BLOCK_SCALED["b"])
+    aq, _, sa = fm.quantize(dev_bf16(a), fm.E4M3, fm.ROW_1x128)
+    bq, _, sb = fm.quantize(dev_bf16(b), fm.E4M3, fm.BLOCK_128x128)
+    y = host(fm.scaled_mm(aq, 0, sa, fm.ROW_1x128, bq, 0, sb, fm.BLOCK_128x128))
+    g = np.random.default_rng(4)
+    _check_points(y, host(aq), 0, host(sa), 1, host(bq), 0, host(sb), 2, g, "block-scaled 16384")
+
+
+def test_backward_workload_sampled():
+    """dY [65536,3072] ~N(0,1e-3) -> E5M2 with its transpose; X, W of the
+    speedrun forward in E4M3; dX = dY W and dW = dY^T X."""
+    x = synth.normal_bf16(3, 0, synth.SPEEDRUN_UP_PROJ["x"], 1.0)
+    w = synth.normal_bf16(3, 1, synth.SPEEDRUN_UP_PROJ["w"], 0.02)
+    dy = synth.normal_bf16(5, 0, synth.UP_PROJ_BACKWARD["dy"], 1e-3)
+    ctr = fm.Counters()
+    dyq, dyqt, dys = fm.quantize(dev_bf16(dy), fm.E5M2, want_t=True, counters=ctr)
+    xq, xqt, xs = fm.quantize(dev_bf16(x), fm.E4M3, want_t=True, counters=ctr)
+    wq, wqt, ws = fm.quantize(dev_bf16(w), fm.E4M3, want_t=True, counters=ctr)
+    dx = host(fm.scaled_mm(dyq, 1, dys, 0, wqt, 0, ws, 0, counters=ctr))
+    dw = host(fm.scaled_mm(dyqt, 1, dys, 0, xqt, 0, xs, 0, counters=ctr))
+    c = ctr.read()
+    assert c["saturated"] == 0 and c["nan"] == 0 and c["nonfinite_out"] == 0
+    g = np.random.default_rng(5)
+    h_dyq, h_wqt = host(dyq), host(wqt)
+    _check_points(dx, h_dyq, 1, host(dys), 0, h_wqt, 0, host(ws), 0, g, "dX")
+    _check_points(dw, host(dyqt), 1, host(dys), 0, host(xqt), 0, host(xs), 0, g, "dW")
+    # the transposed copies are the byte transposes of the codes
+    assert np.array_equal(host(wqt), host(wq).T)
+    odq, _, ods, oc = oracle.quantize(dy, fm.E5M2)
+    assert np.array_equal(h_dyq, odq) and host(dys)[0] == ods[0]

@@ -1,0 +1,181 @@
+"""GPU parity of the quantizers against the oracle: bytes, scales and counters
+bit-exact, on every bf16 bit pattern, on many amax-derived scales, on ragged,
+strided and empty shapes, and on the full 8192 x 8192 quantize workload."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_matmul_amd as fm
+import oracle
+import synth
+from gpu_util import dev_bf16, dev_f32, gpu_quantize, host, same_counters
+
+pytestmark = pytest.mark.gpu
+FMTS = [fm.E4M3, fm.E5M2]
+SCALES = [1.0, 2.0 ** -10, 0.5, 3.0, 1.0 / 448.0, 1.0 / 57344.0, 4.5 / 448.0, 5000.0 / 448.0,
+          5000.0 / 57344.0, 0.0213 / 448.0, 1.1920929e-7, 7.3e-3, 1e-30, 3e30]
+
+
+def _cmp(x_bits, fmt, gran, mode=fm.FROM_AMAX, scale=None, want_t=False, x_dev=None, x_orc=None):
+    xd = x_dev if x_dev is not None else dev_bf16(x_bits)
+    q, qt, s, c = gpu_quantize(xd, fmt, gran, mode, scale, want_t)
+    oq, oqt, os_, oc = oracle.quantize(x_orc if x_orc is not None else x_bits, fmt, gran, mode, scale, want_t)
+    assert np.array_equal(s.reshape(os_.shape), os_), "scales differ"
+    bad = np.nonzero(q != oq)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}: gpu {q[bad][0]:#x} oracle {oq[bad][0]:#x}"
+    if want_t:
+        assert np.array_equal(qt, oqt), "transposed codes differ"
+    assert same_counters(c, oc), f"counters gpu {c} oracle {oc}"
+    return c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("s", SCALES)
+def test_every_bf16_pattern_given_scale(fmt, s):
+    x = synth.all_bf16_patterns()
+    _cmp(x, fmt, fm.TENSOR, fm.GIVEN, np.float32([s]))
+    _cmp(x, fmt, fm.TENSOR, fm.GIVEN, np.float32([s]), want_t=True)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_bf16_pattern_from_amax(fmt):
+    """With Inf/NaN present the kernels take the general branch."""
+    _cmp(synth.all_bf16_patterns(), fmt, fm.TENSOR)
+
+
+AMAXES = [0x7F7F, 0x7F00, 0x4700, 0x43E0, 0x3F80, 0x3C00, 0x2000, 0x1F80, 0x0100, 0x0080, 0x0040, 0x0001]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("amax_bits", AMAXES)
+def test_from_amax_every_finite_pattern_below_amax(fmt, amax_bits):
+    """Fast branch (finite inputs): every bf16 pattern with |x| <= amax."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mag = pats & 0x7FFF
+    x = pats[mag <= amax_bits]
+    pad = (-x.size) % 256
+    x = np.concatenate([x, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 256)
+    _cmp(x, fmt, fm.TENSOR)
+    _cmp(x, fmt, fm.TENSOR, want_t=True)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_row_tiles_thousands_of_scales(fmt):
+    """Each 1x128 tile has its own amax, spread over the whole bf16 range, so
+    one call exercises thousands of scales."""
+    g = np.random.default_rng(11)
+    rows, tiles = 512, 12
+    x = g.integers(0, 65536, size=(rows, tiles * 128)).astype(np.uint16)
+    exp = g.integers(1, 0xFF, size=(rows, tiles, 1)).astype(np.uint16)
+    xs = x.reshape(rows, tiles, 128)
+    xs = (xs & 0x807F) | (np.minimum(exp, ((xs >> 7) & 0xFF)) << 7).astype(np.uint16)
+    x = xs.reshape(rows, tiles * 128)
+    _cmp(x, fmt, fm.ROW_1x128)
+    # with a few non-finite values sprinkled in (general branch for those tiles)
+    x2 = x.copy()
+    x2[g.integers(0, rows, 40), g.integers(0, tiles * 128, 40)] = 0x7F80
+    x2[g.integers(0, rows, 40), g.integers(0, tiles * 128, 40)] = 0xFFC1
+    _cmp(x2, fmt, fm.ROW_1x128)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (200, 300), (1, 5), (129, 127), (7, 1000)])
+def test_block_128_and_transpose(fmt, shape):
+    x = synth.with_outliers_bf16(2, shape, frac=0.01)
+    _cmp(x, fmt, fm.BLOCK_128x128)
+    _cmp(x, fmt, fm.BLOCK_128x128, want_t=True)
+    sc = np.random.default_rng(3).uniform(0.001, 10, size=oracle.scale_shape(2, *shape)).astype(np.float32)
+    _cmp(x, fmt, fm.BLOCK_128x128, fm.GIVEN, sc, want_t=True)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 1), (3, 17), (64, 128), (100, 1000), (257, 130), (1024, 768)])
+def test_ragged_shapes_all_granularities(fmt, shape):
+    x = synth.with_outliers_bf16(5, shape, frac=0.02)
+    _cmp(x, fmt, fm.TENSOR)
+    _cmp(x, fmt, fm.TENSOR, want_t=True)
+    _cmp(x, fmt, fm.ROW_1x128)
+    sc = np.random.default_rng(4).uniform(0.001, 10, size=oracle.scale_shape(1, *shape)).astype(np.float32)
+    _cmp(x, fmt, fm.ROW_1x128, fm.GIVEN, sc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp32_master_input(fmt):
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((300, 520)) * 0.02).astype(np.float32)
+    x[0, 0] = 3e-41                  # fp32 subnormal
+    x[1, 1] = -0.0
+    for gran, want_t in [(fm.TENSOR, False), (fm.TENSOR, True), (fm.BLOCK_128x128, True), (fm.ROW_1x128, False)]:
+        _cmp(None, fmt, gran, want_t=want_t, x_dev=dev_f32(x), x_orc=x)
+
+
+def test_strided_inputs_and_outputs():
+    x_full = synth.with_outliers_bf16(6, (96, 400), frac=0.02)
+    x = dev_bf16(x_full)[:, 16:336]           # ld 400 > cols 320
+    xo = np.ascontiguousarray(x_full[:, 16:336])
+    for gran in (fm.TENSOR, fm.ROW_1x128, fm.BLOCK_128x128):
+        out = torch.full((96, 352), 0xAA, dtype=torch.uint8, device="cuda")
+        ctr = fm.Counters()
+        q, _, s = fm.quantize(x, fm.E4M3, gran, fm.FROM_AMAX, out=out[:, :320], counters=ctr)
+        oq, _, os_, oc = oracle.quantize(xo, fm.E4M3, gran)
+        got = host(out)
+        assert np.array_equal(got[:, :320], oq)
+        assert np.all(got[:, 320:] == 0xAA), "wrote past cols"
+        assert np.array_equal(host(s).reshape(os_.shape), os_)
+
+
+def test_empty_and_degenerate():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, _, s = fm.quantize(x, fm.E4M3)
+    assert q.shape == (0, 64) and host(s)[0] == 1.0
+    z = synth.f32_to_bf16_bits(np.zeros((16, 256), np.float32))
+    _cmp(z, fm.E4M3, fm.TENSOR)                      # amax 0 -> scale 1
+    _cmp(z, fm.E5M2, fm.ROW_1x128)
+    nan = np.full((4, 128), 0x7FC0, dtype=np.uint16)
+    _cmp(nan, fm.E4M3, fm.TENSOR)                    # all NaN
+    _cmp(nan, fm.E4M3, fm.BLOCK_128x128)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_amax_entry_point(fmt):
+    x = synth.with_outliers_bf16(7, (300, 700), frac=0.01)
+    xd = dev_bf16(x)
+    for gran in (fm.TENSOR, fm.ROW_1x128, fm.BLOCK_128x128):
+        got = host(fm.amax(xd, gran))
+        assert np.array_equal(got.reshape(-1), oracle.amax(x, gran).reshape(-1)), gran
+
+
+def test_hardware_conversion_sweep():
+    """fp32 inputs with scale 1 (the quotient is the input): every combination
+    of sign, exponent 2^-20 .. 2^16, top 12 mantissa bits and a set of low
+    (sticky) bit patterns, so every rounding decision of both formats is met."""
+    lows = np.array([0, 1, 2, 0x3FF, 0x400, 0x401, 0x7FE, 0x7FF, 0x155, 0x6AA], dtype=np.uint32)
+    exps = np.arange(127 - 20, 127 + 17, dtype=np.uint32)
+    top = np.arange(4096, dtype=np.uint32)
+    bits = (exps[:, None, None] << 23) | (top[None, :, None] << 11) | lows[None, None, :]
+    bits = np.concatenate([bits.reshape(-1), bits.reshape(-1) | 0x80000000]).astype(np.uint32)
+    pad = (-bits.size) % 1024
+    bits = np.concatenate([bits, np.zeros(pad, np.uint32)])
+    x = bits.view(np.float32).reshape(-1, 1024)
+    for fmt in FMTS:
+        _cmp(None, fmt, fm.TENSOR, fm.GIVEN, np.float32([1.0]), x_dev=dev_f32(x), x_orc=x)
+
+
+def test_deterministic_repeat():
+    x = synth.with_outliers_bf16(8, (1024, 1024))
+    xd = dev_bf16(x)
+    a = gpu_quantize(xd, fm.E5M2, fm.TENSOR, want_t=True)
+    b = gpu_quantize(xd, fm.E5M2, fm.TENSOR, want_t=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[3] == b[3]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("gran", [fm.TENSOR, fm.ROW_1x128])
+def test_quantize_only_workload_full_size(fmt, gran):
+    """8192 x 8192 bf16, N(0,1) with 0.1% +-U(500,5000) outliers: bytes,
+    scales and saturation/underflow counts bit-exact."""
+    x = synth.with_outliers_bf16(2, synth.QUANT_ONLY["x"])
+    c = _cmp(x, fmt, gran)
+    assert c["saturated"] == 0 and c["nan"] == 0
+    if gran == fm.TENSOR and fmt == fm.E4M3:
+        assert c["underflow"] > 100000      # scale ~11: many N(0,1) values underflow
