@@ -136,6 +136,9 @@ uint8_t orc_cast_one(int fmt, float x, float s, orc_counters* ctr)
     volatile float v = x / s;   /* one correctly rounded fp32 division */
     int ev;
     uint8_t c = orc_encode(fmt, v, x != 0.0f, &ev);
+    /* IEEE 754 leaves the sign of a NaN result unspecified; the NaN code takes
+     * the sign the quotient would have, sign(x) xor sign(s). */
+    if (ev == ORC_EV_NAN) c = (uint8_t)(((signbit(x) != 0) != (signbit(s) != 0) ? 0x80 : 0) | 0x7F);
     count_event(ctr, ev);
     return c;
 }

@@ -62,7 +62,8 @@ double orc_decode(int fmt, uint8_t code);
  * of ORC_EV_*. */
 uint8_t orc_encode(int fmt, float v, int src_nonzero, int* event);
 
-/* Quantize one element: v = fl32(x/s) (IEEE fp32 division), then orc_encode. */
+/* Quantize one element: v = fl32(x/s) (IEEE fp32 division), then orc_encode;
+ * a NaN quotient gets the code 0x7F with sign(x) xor sign(s). */
 uint8_t orc_cast_one(int fmt, float x, float s, orc_counters* ctr);
 
 /* Read element idx of a bf16 (uint16 bit pattern) or fp32 array as fp32. */
