@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8mi.so")
 
-SOURCES = ["quantize.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "gemm_persistent.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

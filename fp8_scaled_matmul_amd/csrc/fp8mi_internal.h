@@ -56,6 +56,8 @@ struct GemmArgs {
 };
 
 int gemm_choose_splits(int64_t m, int64_t n, int64_t k);
+int gemm_num_cus();
+hipError_t launch_gemm_persistent(const GemmArgs& g, int num_cus, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8mi

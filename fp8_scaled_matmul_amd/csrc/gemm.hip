@@ -63,33 +63,49 @@ struct KArgs {
     fp8_counters* ctr;
 };
 
-// Global -> register staging of one 256x128 operand tile: thread t loads
-// chunks (row t/8 + 32 i, chunk t%8), i = 0..7; rows past `rows` and K past
-// `k` read as zero.
-__device__ inline void load_tile(const uint8_t* base, int64_t ld, int row0, int rows, int k0, int k,
-                                 uint4 regs[8])
+// Operand tiles move from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds: one instruction fills 1 KB (8 rows of 128
+// bytes) at the wave-uniform LDS address in M0, lane l writing bytes
+// 16 l .. 16 l + 15.  Wave w fills rows 64 w .. 64 w + 63 with 8
+// instructions; the swizzle is applied on the global side by choosing which
+// 16-byte chunk each lane fetches.  Rows past the operand's end fall outside
+// the buffer descriptor's range, and K chunks past k are given an offset
+// outside it: the range check makes both read as zero, with no branches.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct TileLoader {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff[8];   // byte offset of this lane's chunk for instruction j, at k0 = 0
+    int ck[2];          // K byte offset of that chunk within a K step (depends on j & 1 only)
+};
+
+__device__ inline TileLoader make_loader(const uint8_t* base, int64_t ld, int row0, int rows)
 {
-    const int t = threadIdx.x;
-    const int c = t & 7;
-    const int kk = k0 + c * 16;
+    TileLoader L;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int64_t left = (int64_t)rows - row0;
+    const int64_t nrec = left <= 0 ? 0 : std::min<int64_t>(left, BM) * ld;
+    L.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + (int64_t)row0 * ld), (short)0,
+                                               (int)std::min<int64_t>(nrec, 0x7FFFFFF0), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (t >> 3) + 32 * i;
-        if (row0 + r < rows && kk < k)
-            regs[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(row0 + r) * ld + kk);
-        else
-            regs[i] = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+        const int r = 64 * w + 8 * j + (l >> 3);
+        const int c = swz(r, l & 7);      // the swizzle is its own inverse
+        L.voff[j] = (uint32_t)(r * ld + 16 * c);
+        if (j < 2) L.ck[j] = 16 * c;
     }
+    return L;
 }
 
-__device__ inline void store_tile(uint8_t* lds, const uint4 regs[8])
+__device__ inline void issue_tile(const TileLoader& L, uint8_t* lds_tile, int k0, int k)
 {
-    const int t = threadIdx.x;
-    const int c = t & 7;
+    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (t >> 3) + 32 * i;
-        *reinterpret_cast<uint4*>(lds + r * BK + swz(r, c) * 16) = regs[i];
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t off = k0 + L.ck[j & 1] < k ? L.voff[j] + (uint32_t)k0 : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsrc,
+                                                 (__attribute__((address_space(3))) void*)(lds_tile + (w * 8 + j) * 1024),
+                                                 16, (int)off, 0, 0, 0);
     }
 }
 
@@ -136,13 +152,17 @@ __device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn)
     tn = r / gsize;
 }
 
+__shared__ __attribute__((aligned(1024))) uint8_t g_lds_a[2 * kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) float g_lds_sa[2 * BM];
+
+// Per K step and wave: read all 16 operand fragments of the current stage,
+// then start the DMA of the next stage, then run the 64 MFMAs.  Reading
+// before the DMA is issued keeps the compiler from making the reads wait for
+// the DMA (it cannot tell the two stages apart).
 template <int FA, int FB, bool BLOCK>
 __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTileBytes];
-    __shared__ float lds_sa[2][BM];
-
     int split, tm, tn;
     tile_of(p, split, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -155,6 +175,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
     const int wm = (wave >> 1) * 128;
     const int wn = (wave & 1) * 128;
     const int nkb = p.k / BK;   // block-scale columns (k % 128 == 0 in block mode)
+    const int nb = (n0 + wn) / 128;
+    const bool wave_has_cols = n0 + wn < p.n;
 
     v4f acc[8][8];
 #pragma unroll
@@ -162,52 +184,52 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 ra[8], rb[8];
-    float rsa = 0.0f;
+    const TileLoader la_ = make_loader(p.a, p.lda, m0, p.m);
+    const TileLoader lb_ = make_loader(p.b, p.ldb, n0, p.n);
     if (kt0 < kt1) {
-        load_tile(p.a, p.lda, m0, p.m, kt0 * BK, p.k, ra);
-        load_tile(p.b, p.ldb, n0, p.n, kt0 * BK, p.k, rb);
+        issue_tile(la_, g_lds_a, kt0 * BK, p.k);
+        issue_tile(lb_, g_lds_b, kt0 * BK, p.k);
         if constexpr (BLOCK)
-            rsa = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt0] : 0.0f;
-        store_tile(lds_a[0], ra);
-        store_tile(lds_b[0], rb);
-        if constexpr (BLOCK) lds_sa[0][threadIdx.x] = rsa;
+            g_lds_sa[threadIdx.x] = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt0] : 0.0f;
     }
-    __syncthreads();
-
     for (int kt = kt0; kt < kt1; ++kt) {
         const int buf = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
-        if (more) {
-            load_tile(p.a, p.lda, m0, p.m, (kt + 1) * BK, p.k, ra);
-            load_tile(p.b, p.ldb, n0, p.n, (kt + 1) * BK, p.k, rb);
-            if constexpr (BLOCK)
-                rsa = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt + 1] : 0.0f;
-        }
-        const uint8_t* la = lds_a[buf];
-        const uint8_t* lb = lds_b[buf];
-        v8i bf[8];
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const uint8_t* la = g_lds_a + buf * kTileBytes;
+        const uint8_t* lb = g_lds_b + buf * kTileBytes;
+        v8i bf[8], af[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) bf[j] = load_frag(lb, wn + 16 * j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = load_frag(la, wm + 16 * i);
+        float4 sa4[8];
+        float sbv = 0.0f;
+        if constexpr (BLOCK) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sa4[i] = *reinterpret_cast<const float4*>(&g_lds_sa[buf * BM + wm + 16 * i + 4 * (lane >> 4)]);
+            sbv = wave_has_cols ? p.sb[(int64_t)nb * nkb + kt] : 0.0f;
+        }
+        if (kt + 1 < kt1) {
+            issue_tile(la_, g_lds_a + (buf ^ 1) * kTileBytes, (kt + 1) * BK, p.k);
+            issue_tile(lb_, g_lds_b + (buf ^ 1) * kTileBytes, (kt + 1) * BK, p.k);
+            if constexpr (BLOCK)
+                g_lds_sa[(buf ^ 1) * BM + threadIdx.x] =
+                    (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt + 1] : 0.0f;
+        }
         if constexpr (!BLOCK) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const v8i af = load_frag(la, wm + 16 * i);
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af, bf[j], acc[i][j]);
-            }
+                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af[i], bf[j], acc[i][j]);
         } else {
-            // s_b of this wave's 128 columns and this K block (uniform)
-            const int nb = (n0 + wn) / 128;
-            const float sbv = (n0 + wn < p.n) ? p.sb[(int64_t)nb * nkb + kt] : 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const v8i af = load_frag(la, wm + 16 * i);
-                const float4 sa4 = *reinterpret_cast<const float4*>(&lds_sa[buf][wm + 16 * i + 4 * (lane >> 4)]);
-                const float c0 = sa4.x * sbv, c1 = sa4.y * sbv, c2 = sa4.z * sbv, c3 = sa4.w * sbv;
+                const float c0 = sa4[i].x * sbv, c1 = sa4[i].y * sbv, c2 = sa4[i].z * sbv, c3 = sa4[i].w * sbv;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const v4f part = mfma<FA, FB>(af, bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                    const v4f part = mfma<FA, FB>(af[i], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
                     acc[i][j][0] = __builtin_fmaf(part[0], c0, acc[i][j][0]);
                     acc[i][j][1] = __builtin_fmaf(part[1], c1, acc[i][j][1]);
                     acc[i][j][2] = __builtin_fmaf(part[2], c2, acc[i][j][2]);
@@ -215,12 +237,6 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
                 }
             }
         }
-        if (more) {
-            store_tile(lds_a[buf ^ 1], ra);
-            store_tile(lds_b[buf ^ 1], rb);
-            if constexpr (BLOCK) lds_sa[buf ^ 1][threadIdx.x] = rsa;
-        }
-        __syncthreads();
     }
 
     // epilogue: lane holds column n0+wn+16j+lane%16, rows m0+wm+16i+4(lane/16)+r
@@ -302,6 +318,20 @@ hipError_t gemm_fmt(const KArgs& p, bool block, int grid, hipStream_t stream)
 
 }  // namespace
 
+int gemm_num_cus()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 // Split K when the output has too few 256x256 tiles to fill the 256 CUs and
 // each split keeps at least 8 K steps.
 int gemm_choose_splits(int64_t m, int64_t n, int64_t k)
@@ -348,8 +378,17 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         p.splits = (p.ktiles + kt_per - 1) / kt_per;
         if (p.splits == 1) p.ws = nullptr;
     }
-    const int grid = p.tiles_m * p.tiles_n * p.splits;
     hipError_t e;
+    if (!g.block_scaled) {
+        e = launch_gemm_persistent(g, gemm_num_cus(), stream);
+        if (e != hipSuccess || !p.ws) return e;
+        const int64_t total = g.m * g.n;
+        const int rgrid = (int)std::min<int64_t>((total + 255) / 256, 8192);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3(rgrid), dim3(256), 0, stream, p.ws, p.splits, p.m, p.n, 1.0f,
+                           g.sa, g.sb, p.c, g.ldc, g.ctr);
+        return hipGetLastError();
+    }
+    const int grid = p.tiles_m * p.tiles_n * p.splits;
     if (g.fa == FP8_E4M3)
         e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, g.block_scaled, grid, stream)
                              : gemm_fmt<0, 1>(p, g.block_scaled, grid, stream);
