@@ -231,6 +231,9 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda, const flo
     if (m > 0 && n > 0 && !c_bf16) return fail(FP8_ERR_INVALID_ARG, "c: null pointer");
     if (m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "dimensions must be below 2^31");
+    // byte offsets inside one 256-row operand or output tile are 32-bit
+    if (reads && (lda >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 22) || ldc >= ((int64_t)1 << 21)))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "lda, ldb must be below 2^22 and ldc below 2^21");
     if (m > 0 && n > 0 && k > 0 && (!scale_a || !scale_b)) return fail(FP8_ERR_INVALID_ARG, "scale: null pointer");
     if ((s = check_device()) != FP8_OK) return s;
     GemmArgs g;

@@ -139,6 +139,7 @@ __device__ inline void barrier_only()
 // waits until at most n of this wave's vector memory operations are pending.
 __device__ inline void wait_vmcnt(int n)
 {
+    n = __builtin_amdgcn_readfirstlane(n);   // uniform: scalar branches only
     if (n >= 48) {
         if (n >= 63) asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
         else if (n >= 56) asm volatile("s_waitcnt vmcnt(56)" ::: "memory");

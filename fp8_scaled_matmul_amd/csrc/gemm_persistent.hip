@@ -4,23 +4,32 @@
 // Precision", code excerpt and "Explanation"), or, for a K split, the fp32
 // partial sums of one K range.
 //
-// One workgroup of 4 waves per CU walks a list of 256x256 output tiles.  The
-// list of each XCD is a contiguous, M-grouped range, so the A panels and the
-// B operand a wave of workgroups shares sit in that XCD's L2.  The K steps
-// of all the workgroup's tiles form one stream: step q's operands (two
-// 32 KB tiles) arrive in LDS stage q%2 by DMA issued two steps earlier, so
-// the first steps of the next tile load while the current tile finishes and
-// writes its output.  Per step and wave: read the 16 MFMA fragments of the
-// stage into registers, release the stage, start the DMA of step q+2 into
-// it, run 64 MFMAs (16x16x128) into 256 fp32 accumulators.
+// One workgroup of 4 waves per CU walks a list of 256x256 output tiles (each
+// wave owns 128x128).  The list of each XCD is a contiguous, M-grouped range,
+// so the A panels and the B operand that the XCD's workgroups share stay in
+// its L2.  The K dimension of all the workgroup's tiles forms one stream of
+// 64-deep half steps; each half step is 16 v_mfma_scale_f32_32x32x64_f8f6f4
+// per wave.
 //
-// Output layout trick: B rows are placed in LDS so that MFMA lane p of
-// column fragment j holds output column 8p + j.  Each lane then owns eight
-// consecutive columns of every output row it touches, and the epilogue
-// writes a row segment with one 16-byte store.
+// Pipeline (the LDS read bandwidth is what has to be hidden):
+//   - 4 LDS stages of 32 KB (A and B, 64 K each); the DMA of half step t+4
+//     (buffer_load ... lds, waited for with counted vmcnt) refills the stage
+//     half step t has just released;
+//   - two fragment register sets: while the 16 MFMAs of half step t run, the
+//     16 ds_read_b128 of half step t+1 are issued between them;
+//   - one barrier per half step.
+// The next tile's first half steps load while the current tile's epilogue
+// writes its output.
+//
+// Output layout: B rows are placed in LDS so that MFMA lane p of column
+// fragment j holds output column 4p + j; each lane owns four consecutive
+// columns of every output row it touches (one 8-byte bf16 store, or one
+// 16-byte fp32 store, per row).
 #include "device_common.h"
 #include "fp8mi_internal.h"
 #include "gemm_common.h"
+
+#include <type_traits>
 
 namespace fp8mi {
 
@@ -29,6 +38,16 @@ using namespace gemm;
 namespace {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+constexpr int KH = 64;                      // K bytes per half step (one stage)
+constexpr int kStages = 4;
+constexpr int kStageBytes = BM * KH;        // 16 KB per operand per stage
+constexpr int kDmaPerHalf = 8;              // DMA instructions per thread per half step
+constexpr int kStoresBf16 = 64;             // epilogue stores per thread, bf16 output
+constexpr int kStoresF32 = 64;              // fp32 split partials
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutGeneric = 2;
 
 struct PArgs {
     const uint8_t* a;
@@ -40,18 +59,58 @@ struct PArgs {
     uint16_t* c;
     int64_t ldc;
     float* ws;          // split partials [splits][m][n] fp32, or nullptr
-    int splits, kt_per, ktiles;
+    int splits, h_per, nhalves;
     int tiles_m, tiles_n;
     int items, per_xcd, g8;
-    int fast_store;     // 16-byte row-segment stores are aligned and in range
+    int fast_store;     // row-segment stores are aligned and in range
     fp8_counters* ctr;
 };
 
-__shared__ __attribute__((aligned(1024))) uint8_t p_lds_a[2 * kTileBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t p_lds_b[2 * kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_lds_a[kStages * kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_lds_b[kStages * kStageBytes];
+
+// 16-byte chunk c (0..3) of the 64-byte LDS row r sits at position
+// swz4(r, c).  For 8 aligned consecutive rows reading the same chunk the
+// (row parity, position) pairs are distinct (no conflict with 32 banks), and
+// so are the (row mod 4, position) pairs of 16 aligned rows (64 banks).  An
+// involution.
+__device__ inline int swz4(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
+
+template <int FA, int FB>
+__device__ inline v16f mfma32(const v8i& a, const v8i& b, const v16f& c)
+{
+    // unit block scales: E8M0 exponent 127 = 2^0; FA / FB: 0 = E4M3, 1 = E5M2
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+}
+
+// 32x64 operand fragment of one stage: lane l reads row row0 + l%32, K bytes
+// 32 (l/32) .. +32 (A and B alike, so the products pair up whatever order the
+// instruction gives the 64 K values).
+__device__ inline v8i frag32(const uint8_t* stage, int row0)
+{
+    const int l = threadIdx.x & 63;
+    const int r = row0 + (l & 31);
+    const int c0 = (l >> 5) * 2;
+    const uint4 lo = *reinterpret_cast<const uint4*>(stage + r * KH + swz4(r, c0) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(stage + r * KH + swz4(r, c0 + 1) * 16);
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+}
+
+// The accumulators live in AGPRs; an arithmetic use needs a copy into a
+// VGPR.  Issuing it here keeps the compiler from copying all 256 at once
+// (which runs out of VGPRs) at the end of the K loop.
+__device__ inline float agpr_read(float a)
+{
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
 
 struct Item {
-    int m0, n0, kt0, kt1, split;
+    int m0, n0, h0, h1, split;
 };
 
 __device__ inline Item decode_item(const PArgs& p, int item)
@@ -65,26 +124,21 @@ __device__ inline Item decode_item(const PArgs& p, int item)
     const int first_m = g * kGroupM;
     const int gsize = min(p.tiles_m - first_m, kGroupM);
     const int r = t - g * in_group;
-    it.m0 = (first_m + r % gsize) * BM;
-    it.n0 = (r / gsize) * BN;
-    it.kt0 = it.split * p.kt_per;
-    it.kt1 = min(p.ktiles, it.kt0 + p.kt_per);
     // all of it is uniform over the workgroup: keep it in scalar registers
-    it.m0 = __builtin_amdgcn_readfirstlane(it.m0);
-    it.n0 = __builtin_amdgcn_readfirstlane(it.n0);
-    it.kt0 = __builtin_amdgcn_readfirstlane(it.kt0);
-    it.kt1 = __builtin_amdgcn_readfirstlane(it.kt1);
+    it.m0 = __builtin_amdgcn_readfirstlane((first_m + r % gsize) * BM);
+    it.n0 = __builtin_amdgcn_readfirstlane((r / gsize) * BN);
+    it.h0 = __builtin_amdgcn_readfirstlane(it.split * p.h_per);
+    it.h1 = __builtin_amdgcn_readfirstlane(min(p.nhalves, it.h0 + p.h_per));
     it.split = __builtin_amdgcn_readfirstlane(it.split);
     return it;
 }
 
-// Position of one workgroup in its stream of (item, K step).
+// Position of one workgroup in its stream of (item, half step).
 struct Cursor {
     int s;          // index in this workgroup's item list
     int item_end;   // end of this XCD's item range
-    int item;
     Item it;
-    int kt;
+    int h;
     bool valid;
 };
 
@@ -93,28 +147,29 @@ __device__ inline void cursor_load(const PArgs& p, Cursor& c, int xcd, int slot)
     const int item = __builtin_amdgcn_readfirstlane(xcd * p.per_xcd + slot + p.g8 * c.s);
     c.valid = item < c.item_end;
     if (c.valid) {
-        c.item = item;
         c.it = decode_item(p, item);
-        c.kt = c.it.kt0;
+        c.h = c.it.h0;
     }
 }
 
 __device__ inline void cursor_next(const PArgs& p, Cursor& c, int xcd, int slot)
 {
-    if (++c.kt >= c.it.kt1) {
+    if (++c.h >= c.it.h1) {
         ++c.s;
         cursor_load(p, c, xcd, slot);
     }
 }
 
-// Per-lane byte offsets of the 8 DMA chunks of one operand tile (tile base
-// and K offset excluded).  Wave w fills LDS rows 64 w .. 64 w + 63; LDS slot
-// (row R, position l%8) receives the logical chunk swz(R, l%8) of global
-// row g(R).  A: g(R) = R.  B: within each 128-row half, g(R) = 8 (R%16) + R/16,
-// so that fragment j's lane p (LDS row 16 j + p) holds column 8 p + j.
+// Per-lane byte offsets of the 4 DMA instructions per operand and half step
+// of this wave: instruction j fills LDS rows 64 w + 16 j .. +15; lane l
+// writes row R = 64 w + 16 j + l/4, position l%4, which receives logical
+// chunk swz4(R, l%4) of global row g(R).  A: g(R) = R.  B: within each
+// 128-row half, g(R) = 4 (R%32) + R/32, so that fragment j's lane p (LDS row
+// 32 j + p) carries output column 4 p + j.  The chunk index does not depend
+// on j (16 j and 64 w do not change the swizzle).
 struct Offsets {
-    uint32_t voff[8];
-    int ck[2];      // K byte offset of the chunk, for instruction parity j & 1
+    uint32_t voff[4];
+    int ck;         // K byte offset of this lane's chunk
 };
 
 __device__ inline Offsets make_offsets(int64_t ld, bool permute)
@@ -122,31 +177,59 @@ __device__ inline Offsets make_offsets(int64_t ld, bool permute)
     Offsets o;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int R = 64 * w + 8 * j + (l >> 3);
-        const int c = swz(R, l & 7);
-        const int g = permute ? (R & 128) + 8 * (R & 15) + ((R & 127) >> 4) : R;
+    for (int j = 0; j < 4; ++j) {
+        const int R = 64 * w + 16 * j + (l >> 2);
+        const int c = swz4(R, l & 3);
+        const int g = permute ? (R & 128) + 4 * (R & 31) + ((R & 127) >> 5) : R;
         o.voff[j] = (uint32_t)(g * ld + 16 * c);
-        if (j < 2) o.ck[j] = 16 * c;
+        if (j == 0) o.ck = 16 * c;
     }
     return o;
 }
 
-__device__ inline void dma_tile(const Offsets& o, const v4u& rsrc, uint32_t lds_base, int k0, int k)
+// k is a multiple of 16: a chunk is entirely inside K or entirely past it
+// (then its offset is out of range and the DMA writes zeros).
+__device__ inline void dma_half(const Offsets& o, const v4u& rsrc, uint32_t lds_stage, int k0, int k)
 {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool in_k = k0 + o.ck < k;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t off = k0 + o.ck[j & 1] < k ? o.voff[j] + (uint32_t)k0 : kOutOfRange;
-        dma16(lds_base + (uint32_t)(w * 8 + j) * 1024u, off, rsrc);
-    }
+    for (int j = 0; j < 4; ++j)
+        dma16(lds_stage + (uint32_t)(w * 4 + j) * 1024u, in_k ? o.voff[j] + (uint32_t)k0 : kOutOfRange, rsrc);
 }
 
-constexpr int kOutBf16 = 0, kOutF32 = 1, kOutGeneric = 2;
-
-constexpr int kDmaPerStep = 16;     // DMA instructions per thread per K step
-constexpr int kStoresBf16 = 32;     // epilogue store instructions per thread (bf16 out)
-constexpr int kStoresF32 = 64;      // (fp32 split partials)
+// One half step: 16 MFMAs on the current fragments, with the 16 LDS reads of
+// the next half step's fragments placed between them.
+template <int FA, int FB, bool FIRST>
+__device__ inline void half_step(v16f (&acc)[4][4], const v8i (&ca)[4], const v8i (&cb)[4], v8i (&na)[4],
+                                 v8i (&nb)[4], const uint8_t* la, const uint8_t* lb, int wm, int wn)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (FIRST)
+                acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], v16f{});
+            else
+                acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], acc[i][j]);
+        }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nb[j] = frag32(lb, wn + 32 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) na[i] = frag32(la, wm + 32 * i);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one ds_read
+    }
+    // Pin the MFMAs to this half step: an MFMA touches no memory, so without
+    // a use here the compiler may sink it past the next half step's wait and
+    // barrier.  (Empty asm: no instruction, no wait for the results.)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
 
 template <int FA, int FB, int OUT>
 __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
@@ -154,7 +237,6 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * 128;
     const int wn = (wave & 1) * 128;
 
@@ -166,177 +248,186 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
 
     const Offsets oa = make_offsets(p.lda, false);
     const Offsets ob = make_offsets(p.ldb, true);
-    const uint32_t lds_a0 = lds_addr(p_lds_a), lds_b0 = lds_addr(p_lds_b);
+    const uint32_t lds_a0 = lds_addr(s_lds_a), lds_b0 = lds_addr(s_lds_b);
 
-    const int item_end = min((xcd + 1) * p.per_xcd, p.items);
-    Cursor d;   // DMA cursor, two steps ahead of the compute cursor
+    Cursor d;   // DMA cursor, four half steps ahead of the compute cursor
     d.s = 0;
-    d.item_end = item_end;
+    d.item_end = min((xcd + 1) * p.per_xcd, p.items);
     cursor_load(p, d, xcd, slot);
     Cursor c = d;
+    if (!c.valid) return;
 
-    auto issue = [&](const Cursor& cur, int stage) -> int {
-        if (!cur.valid) return 0;
-        const Item& it = cur.it;
-        const int k0 = cur.kt * BK;
-        const uint32_t ra_bytes = (uint32_t)(min(BM, p.m - it.m0) * p.lda);
-        const uint32_t rb_bytes = (uint32_t)(min(BN, p.n - it.n0) * p.ldb);
-        const v4u ra = make_rsrc(p.a + (int64_t)it.m0 * p.lda, ra_bytes);
-        const v4u rb = make_rsrc(p.b + (int64_t)it.n0 * p.ldb, rb_bytes);
-        dma_tile(oa, ra, lds_a0 + stage * kTileBytes, k0, p.k);
-        dma_tile(ob, rb, lds_b0 + stage * kTileBytes, k0, p.k);
-        return kDmaPerStep;
+    auto issue = [&](int stage) -> int {
+        if (!d.valid) return 0;
+        const Item& it = d.it;
+        const v4u ra = make_rsrc(p.a + (int64_t)it.m0 * p.lda, (uint32_t)(min(BM, p.m - it.m0) * p.lda));
+        const v4u rb = make_rsrc(p.b + (int64_t)it.n0 * p.ldb, (uint32_t)(min(BN, p.n - it.n0) * p.ldb));
+        dma_half(oa, ra, lds_a0 + stage * kStageBytes, d.h * KH, p.k);
+        dma_half(ob, rb, lds_b0 + stage * kStageBytes, d.h * KH, p.k);
+        cursor_next(p, d, xcd, slot);
+        return kDmaPerHalf;
     };
 
-    // prologue: steps 0 and 1 into stages 0 and 1
-    int n_dma_next;            // DMA instructions of the step after the current one
-    issue(d, 0);
-    cursor_next(p, d, xcd, slot);
-    n_dma_next = issue(d, 1);
-    cursor_next(p, d, xcd, slot);
-    int stores_prev2 = 0, stores_prev1 = 0;
+    // prologue: half steps 0..3 into stages 0..3, then the fragments of half 0
+    issue(0);
+    const int dq1 = issue(1);
+    int dq2 = issue(2), dq3 = issue(3);   // DMA counts of half steps t+2, t+3
+    wait_vmcnt(dq1 + dq2 + dq3);
+    barrier_only();
+    v8i ra0[4], rb0[4], ra1[4], rb1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb0[j] = frag32(s_lds_b, wn + 32 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra0[i] = frag32(s_lds_a, wm + 32 * i);
 
+    int s3 = 0, s2 = 0, s1 = 0;    // stores issued in half steps t-3, t-2, t-1
     uint32_t nonfinite = 0;
-    int q = 0;
-    v4f acc[8][8];
-    while (c.valid) {
-      for (bool first = true; ; first = false) {
-        const int stage = q & 1;
-        // step q's DMA is complete once at most the operations issued after
-        // it are pending: the stores of steps q-2 and q-1 and step q+1's DMA
-        wait_vmcnt(stores_prev2 + n_dma_next + stores_prev1);
-        barrier_only();
-        const uint8_t* la = p_lds_a + stage * kTileBytes;
-        const uint8_t* lb = p_lds_b + stage * kTileBytes;
-        v8i af[8], bf[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bf[j] = load_frag(lb, wn + 16 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = load_frag(la, wm + 16 * i);
-        // every wave has its fragments: the stage is free for step q+2
+    v16f acc[4][4];
+    int t = 0;                     // half-step index in this workgroup's stream
+
+    // Half step t: MFMAs on (cur_a, cur_b), fragments of half step t+1 read
+    // into (nxt_a, nxt_b).  Issue order per half step: DMA(t+4), then (after
+    // a tile's last half step) the epilogue's stores, so DMA(t+1), issued in
+    // half step t-3, is complete once at most the stores of t-3..t-1 and
+    // DMA(t+2), DMA(t+3) are pending.
+    auto half = [&](auto first, const v8i (&cur_a)[4], const v8i (&cur_b)[4], v8i (&nxt_a)[4], v8i (&nxt_b)[4]) {
+        wait_vmcnt(dq2 + dq3 + s3 + s2 + s1);
+        // every wave has read its half-t fragments out of stage t%4, and half
+        // t+1's data is in stage (t+1)%4
         barrier_lds();
-        const int n_dma_new = issue(d, stage);
-        cursor_next(p, d, xcd, slot);
-        if (first) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af[i], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        const int dq4 = issue(t & 3);
+        // (after the stream's last half step this reads a stale stage: harmless)
+        const uint8_t* la = s_lds_a + ((t + 1) & 3) * kStageBytes;
+        const uint8_t* lb = s_lds_b + ((t + 1) & 3) * kStageBytes;
+        half_step<FA, FB, decltype(first)::value>(acc, cur_a, cur_b, nxt_a, nxt_b, la, lb, wm, wn);
+        dq2 = dq3;
+        dq3 = dq4;
+        s3 = s2;
+        s2 = s1;
+        s1 = 0;
+        ++t;
+    };
+    using First = std::true_type;
+    using Next = std::false_type;
+
+    while (c.valid) {
+        // the tile's half steps; its fragments start (and end) in set 0
+        const int nh = c.it.h1 - c.it.h0;
+        half(First{}, ra0, rb0, ra1, rb1);
+        int h = 1;
+        for (; h + 2 <= nh; h += 2) {
+            half(Next{}, ra1, rb1, ra0, rb0);
+            half(Next{}, ra0, rb0, ra1, rb1);
+        }
+        if (h < nh) {
+            half(Next{}, ra1, rb1, ra0, rb0);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af[i], bf[j], acc[i][j]);
-        }
-        stores_prev2 = stores_prev1;
-        stores_prev1 = 0;
-        n_dma_next = n_dma_new;
-        ++q;
-        if (c.kt + 1 >= c.it.kt1) break;
-        ++c.kt;
-      }
-        int stores_now = 0;
-        {
-            // epilogue of this tile: lane owns columns n0 + wn + 8 (lane%16) + 0..7
-            // of rows m0 + wm + 16 i + 4 (lane/16) + r
-            const Item& it = c.it;
-            // lane constants recomputed here (pinned by an empty asm) rather
-            // than kept live across the K loop
-            int tid = threadIdx.x;
-            asm volatile("" : "+v"(tid));
-            const int col = it.n0 + ((tid >> 6) & 1) * 128 + 8 * (tid & 15);
-            const int rrow = ((tid >> 7) & 1) * 128 + 4 * ((tid & 63) >> 4);
-            if constexpr (OUT == kOutBf16) {
-                const float scale = out_scale;
-                const __amdgpu_buffer_rsrc_t rs = make_store_rsrc(p.c + (int64_t)it.m0 * p.ldc, (uint32_t)(min(BM, p.m - it.m0) * p.ldc * 2));
-                // running max of |bf16| bit patterns: an exponent field of all ones
-                // (>= 0x7F80) marks Inf / NaN; outputs outside the matrix hold zeros
-                us2 mx = us2{0, 0};
-                // offsets are formed here from one base (an empty asm keeps the
-                // compiler from hoisting 32 of them out of the loop)
-                uint32_t base = col < p.n ? (uint32_t)((rrow * p.ldc + col) * 2) : kOutOfRange;
-                asm volatile("" : "+v"(base));
-                const uint32_t row_bytes = (uint32_t)(p.ldc * 2);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t off = base == kOutOfRange ? kOutOfRange : base + (uint32_t)(16 * i + r) * row_bytes;
-                        v4u v;
-                        v.x = pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
-                        v.y = pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
-                        v.z = pack_bf16(acc[i][4][r] * scale, acc[i][5][r] * scale);
-                        v.w = pack_bf16(acc[i][6][r] * scale, acc[i][7][r] * scale);
-                        store16(v, off, rs);
-                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, v.x & 0x7FFF7FFFu));
-                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, v.y & 0x7FFF7FFFu));
-                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, v.z & 0x7FFF7FFFu));
-                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, v.w & 0x7FFF7FFFu));
-                        if (r == 3) __builtin_amdgcn_sched_barrier(0);
-                    }
-                if (mx.x >= 0x7F80u || mx.y >= 0x7F80u) {
-                    // rare: count exactly
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            if (it.m0 + rrow + 16 * i + r >= p.m || col >= p.n) continue;
-#pragma unroll
-                            for (int j = 0; j < 8; ++j)
-                                nonfinite += (to_bf16(acc[i][j][r] * scale) & 0x7F80u) == 0x7F80u;
-                        }
-                }
-                stores_now = kStoresBf16;
-            } else if constexpr (OUT == kOutF32) {
-                float* wsb = p.ws + ((int64_t)it.split * p.m + it.m0) * p.n;
-                const __amdgpu_buffer_rsrc_t rs = make_store_rsrc(wsb, (uint32_t)(min(BM, p.m - it.m0) * p.n * 4));
-                uint32_t base = col < p.n ? (uint32_t)((rrow * p.n + col) * 4) : kOutOfRange;
-                asm volatile("" : "+v"(base));
-                const uint32_t row_bytes = (uint32_t)(p.n * 4);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t off = base == kOutOfRange ? kOutOfRange : base + (uint32_t)(16 * i + r) * row_bytes;
-                        // (copy the element to a scalar first: a bit cast of an
-                        // ext_vector element expression reads element 0)
-                        uint32_t w[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float f = acc[i][j][r];
-                            w[j] = __builtin_bit_cast(uint32_t, f);
-                        }
-                        store16(v4u{w[0], w[1], w[2], w[3]}, off, rs);
-                        store16(v4u{w[4], w[5], w[6], w[7]}, off + (off == kOutOfRange ? 0u : 16u), rs);
-                        if (r == 3) __builtin_amdgcn_sched_barrier(0);
-                    }
-                stores_now = kStoresF32;
-            } else {
-                // any alignment: element stores, then drain
-                const float scale = out_scale;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = it.m0 + rrow + 16 * i + r;
-                        if (row >= p.m) continue;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            if (col + j >= p.n) continue;
-                            if (p.ws) {
-                                p.ws[((int64_t)it.split * p.m + row) * p.n + col + j] = acc[i][j][r];
-                            } else {
-                                const uint16_t h = to_bf16(acc[i][j][r] * scale);
-                                nonfinite += (h & 0x7F80u) == 0x7F80u;
-                                p.c[(int64_t)row * p.ldc + col + j] = h;
-                            }
-                        }
-                    }
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            for (int i = 0; i < 4; ++i) {
+                ra0[i] = ra1[i];
+                rb0[i] = rb1[i];
             }
         }
-        // the epilogue's stores were issued after step q-1's DMA
-        stores_prev1 = stores_now;
+
+        // epilogue: lane owns columns n0 + wn + 4 (lane%32) + 0..3 of rows
+        // m0 + wm + 32 i + 8 (v/4) + 4 (lane/32) + v%4 (accumulator i, element v)
+        const Item& it = c.it;
+        // lane constants formed here (pinned by an empty asm) rather than
+        // kept live across the K loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int col = it.n0 + ((tid >> 6) & 1) * 128 + 4 * (tid & 31);
+        const int rrow = ((tid >> 7) & 1) * 128 + 4 * ((tid & 63) >> 5);
+        if constexpr (OUT == kOutBf16) {
+            // the reads below are inline asm, which the compiler's hazard
+            // checks do not see: give the last MFMA's results the wait
+            // states an XDL write needs before an AGPR read (at most 19)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            const __amdgpu_buffer_rsrc_t rs =
+                make_store_rsrc(p.c + (int64_t)it.m0 * p.ldc, (uint32_t)(min(BM, p.m - it.m0) * p.ldc * 2));
+            uint32_t base = col < p.n ? (uint32_t)((rrow * p.ldc + col) * 2) : kOutOfRange;
+            asm volatile("" : "+v"(base));
+            const uint32_t row_bytes = (uint32_t)(p.ldc * 2);
+            // running max of |bf16| patterns: >= 0x7F80 marks Inf / NaN
+            // (outputs outside the matrix are zeros: their operands read as zero)
+            us2 mx = us2{0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
+                    const uint32_t off = base == kOutOfRange ? kOutOfRange : base + (uint32_t)rr * row_bytes;
+                    const float e0 = agpr_read(acc[i][0][v]), e1 = agpr_read(acc[i][1][v]);
+                    const float e2 = agpr_read(acc[i][2][v]), e3 = agpr_read(acc[i][3][v]);
+                    v2u w;
+                    w.x = pack_bf16(e0 * out_scale, e1 * out_scale);
+                    w.y = pack_bf16(e2 * out_scale, e3 * out_scale);
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, 0);
+                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.x & 0x7FFF7FFFu));
+                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.y & 0x7FFF7FFFu));
+                    if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            s1 = kStoresBf16;
+            if (mx.x >= 0x7F80u || mx.y >= 0x7F80u) {
+                // rare: count exactly, reading back what this lane stored
+                // (after its stores have completed; the accumulators are
+                // not kept alive for this).  Leaving s1 as it is only
+                // overstates the pending operations of DMAs that this drain
+                // has already completed.
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                for (int i = 0; i < 4; ++i)
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = it.m0 + rrow + 32 * i + 8 * (v >> 2) + (v & 3);
+                        if (row >= p.m || col >= p.n) continue;
+                        const v2u w = *reinterpret_cast<const v2u*>(p.c + (int64_t)row * p.ldc + col);
+                        nonfinite += ((w.x & 0x7F80u) == 0x7F80u) + ((w.x & 0x7F800000u) == 0x7F800000u) +
+                                     ((w.y & 0x7F80u) == 0x7F80u) + ((w.y & 0x7F800000u) == 0x7F800000u);
+                    }
+            }
+        } else if constexpr (OUT == kOutF32) {
+            float* wsb = p.ws + ((int64_t)it.split * p.m + it.m0) * p.n;
+            const __amdgpu_buffer_rsrc_t rs = make_store_rsrc(wsb, (uint32_t)(min(BM, p.m - it.m0) * p.n * 4));
+            uint32_t base = col < p.n ? (uint32_t)((rrow * p.n + col) * 4) : kOutOfRange;
+            asm volatile("" : "+v"(base));
+            const uint32_t row_bytes = (uint32_t)(p.n * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
+                    const uint32_t off = base == kOutOfRange ? kOutOfRange : base + (uint32_t)rr * row_bytes;
+                    // (copy the elements to scalars first: a bit cast of an
+                    // ext_vector element expression reads element 0)
+                    const float e0 = acc[i][0][v], e1 = acc[i][1][v], e2 = acc[i][2][v], e3 = acc[i][3][v];
+                    store16(v4u{__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                                __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)},
+                            off, rs);
+                    if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            s1 = kStoresF32;
+        } else {
+            // any alignment: element stores, then drain
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = it.m0 + rrow + 32 * i + 8 * (v >> 2) + (v & 3);
+                    if (row >= p.m) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (col + j >= p.n) continue;
+                        const float e = acc[i][j][v];
+                        if (p.ws) {
+                            p.ws[((int64_t)it.split * p.m + row) * p.n + col + j] = e;
+                        } else {
+                            const uint16_t hb = to_bf16(e * out_scale);
+                            nonfinite += (hb & 0x7F80u) == 0x7F80u;
+                            p.c[(int64_t)row * p.ldc + col + j] = hb;
+                        }
+                    }
+                }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         ++c.s;
         cursor_load(p, c, xcd, slot);
     }
@@ -362,11 +453,16 @@ hipError_t launch_gemm_persistent(const GemmArgs& g, int num_cus, hipStream_t st
     p.c = static_cast<uint16_t*>(g.c);
     p.ldc = g.ldc;
     p.ctr = g.ctr;
-    p.ktiles = (int)((g.k + BK - 1) / BK);
-    p.splits = g.splits > 1 && g.ws ? g.splits : 1;
-    p.kt_per = (p.ktiles + p.splits - 1) / p.splits;
-    p.splits = (p.ktiles + p.kt_per - 1) / p.kt_per;      // no empty split
-    p.ws = p.splits > 1 ? g.ws : nullptr;
+    p.nhalves = (int)((g.k + KH - 1) / KH);
+    // split ranges in whole 128-deep steps: the split points the workspace
+    // size and the reduce are computed with
+    const int ktiles = (int)((g.k + BK - 1) / BK);
+    int splits = g.splits > 1 && g.ws ? g.splits : 1;
+    const int kt_per = (ktiles + splits - 1) / splits;
+    splits = (ktiles + kt_per - 1) / kt_per;      // no empty split
+    p.splits = splits;
+    p.h_per = 2 * kt_per;
+    p.ws = splits > 1 ? g.ws : nullptr;
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
     p.items = p.tiles_m * p.tiles_n * p.splits;
@@ -382,9 +478,9 @@ hipError_t launch_gemm_persistent(const GemmArgs& g, int num_cus, hipStream_t st
         grid = 8 * p.g8;
     }
     if (p.ws)
-        p.fast_store = (g.n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
+        p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
     else
-        p.fast_store = (g.n % 8 == 0) && (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0);
+        p.fast_store = (g.n % 4 == 0) && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
     const int out = !p.fast_store ? kOutGeneric : (p.ws ? kOutF32 : kOutBf16);
     const int fmt = g.fa * 2 + g.fb;
     switch (fmt * 3 + out) {

@@ -147,7 +147,8 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
  * Products are accumulated in fp32 by the MFMA units; the epilogue rounds to
  * bf16 (nearest even).  Any other pair: FP8_ERR_UNSUPPORTED_SHAPE.
  * Shape rules: k % 16 == 0, lda % 16 == 0, ldb % 16 == 0, a and b 16-byte
- * aligned (else FP8_ERR_UNSUPPORTED_SHAPE); m, n any >= 0; k == 0 writes zeros.
+ * aligned, lda and ldb below 2^22, ldc below 2^21 (else
+ * FP8_ERR_UNSUPPORTED_SHAPE); m, n any >= 0; k == 0 writes zeros.
  * workspace: when fp8_scaled_mm_workspace_size() > 0 the call may split the K
  * dimension into slices reduced in a fixed order (deterministic); a smaller
  * workspace (or NULL) runs without the split (same result to tolerance,

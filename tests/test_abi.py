@@ -100,6 +100,9 @@ def test_quantize_rejects_before_device(L, args, code):
     (dict(k=40, lda=48, ldb=48), fm.FP8_ERR_UNSUPPORTED_SHAPE),                  # k % 16
     (dict(lda=136), fm.FP8_ERR_UNSUPPORTED_SHAPE),                              # lda % 16
     (dict(a=BAD + 8), fm.FP8_ERR_UNSUPPORTED_SHAPE),                            # alignment
+    (dict(lda=1 << 22), fm.FP8_ERR_UNSUPPORTED_SHAPE),                          # 32-bit tile offsets
+    (dict(ldb=1 << 22), fm.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(ldc=1 << 21), fm.FP8_ERR_UNSUPPORTED_SHAPE),
     (dict(lda=64), fm.FP8_ERR_INVALID_ARG),                                     # lda < k
     (dict(ldc=10), fm.FP8_ERR_INVALID_ARG),
     (dict(m=-3), fm.FP8_ERR_INVALID_ARG),
