@@ -140,19 +140,19 @@ __device__ inline void barrier_only()
 __device__ inline void wait_vmcnt(int n)
 {
     n = __builtin_amdgcn_readfirstlane(n);   // uniform: scalar branches only
-    if (n >= 48) {
-        if (n >= 63) asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
-        else if (n >= 56) asm volatile("s_waitcnt vmcnt(56)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-    } else if (n >= 32) {
-        if (n >= 40) asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
-        else if (n >= 33) asm volatile("s_waitcnt vmcnt(33)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    } else if (n >= 16) {
-        if (n >= 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (n >= 63) {
+        asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
+        return;
+    }
+    switch (n >> 3) {   // round down to a multiple of 8 (waits at least as long)
+    case 7: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 }
 

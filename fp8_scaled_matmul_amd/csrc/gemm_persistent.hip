@@ -11,12 +11,14 @@
 // 64-deep half steps; each half step is 16 v_mfma_scale_f32_32x32x64_f8f6f4
 // per wave.
 //
-// Pipeline (the LDS read bandwidth is what has to be hidden):
+// Pipeline (one wave per SIMD, so nothing may stall the MFMA issue):
 //   - 4 LDS stages of 32 KB (A and B, 64 K each); the DMA of half step t+4
 //     (buffer_load ... lds, waited for with counted vmcnt) refills the stage
 //     half step t has just released;
 //   - two fragment register sets: while the 16 MFMAs of half step t run, the
-//     16 ds_read_b128 of half step t+1 are issued between them;
+//     16 ds_read_b128 of half step t+1 and the 8 DMA instructions of half
+//     step t+4 are issued between them (a DMA issue can block while the
+//     address unit is busy; spread out, the queued MFMA covers it);
 //   - one barrier per half step.
 // The next tile's first half steps load while the current tile's epilogue
 // writes its output.
@@ -149,6 +151,9 @@ __device__ inline void cursor_load(const PArgs& p, Cursor& c, int xcd, int slot)
     if (c.valid) {
         c.it = decode_item(p, item);
         c.h = c.it.h0;
+    } else {
+        c.it = Item{0, 0, 0, 0, 0};
+        c.h = 0;
     }
 }
 
@@ -187,40 +192,62 @@ __device__ inline Offsets make_offsets(int64_t ld, bool permute)
     return o;
 }
 
-// k is a multiple of 16: a chunk is entirely inside K or entirely past it
-// (then its offset is out of range and the DMA writes zeros).
-__device__ inline void dma_half(const Offsets& o, const v4u& rsrc, uint32_t lds_stage, int k0, int k)
+// The 8 DMA instructions (4 for A, 4 for B) of one half step of one wave.
+// Once the stream has ended the descriptors have zero length: the loads
+// then write zeros into a stage nothing reads any more, which keeps the
+// count of pending operations the same for every half step.
+struct DmaJob {
+    v4u ra, rb;
+    uint32_t lds_a, lds_b;      // this wave's first 1 KB slot of the stage
+    int k0;
+};
+
+// Instruction j (0..7) of a job.  k is a multiple of 16: a chunk is
+// entirely inside K or entirely past it (then its offset is out of range and
+// the DMA writes zeros).
+__device__ inline void dma_one(const DmaJob& job, const Offsets& oa, const Offsets& ob, int j, int k)
 {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool in_k = k0 + o.ck < k;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        dma16(lds_stage + (uint32_t)(w * 4 + j) * 1024u, in_k ? o.voff[j] + (uint32_t)k0 : kOutOfRange, rsrc);
+    const bool in_k = job.k0 + oa.ck < k;     // (oa.ck == ob.ck)
+    if (j < 4)
+        dma16(job.lds_a + (uint32_t)j * 1024u, in_k ? oa.voff[j] + (uint32_t)job.k0 : kOutOfRange, job.ra);
+    else
+        dma16(job.lds_b + (uint32_t)(j - 4) * 1024u, in_k ? ob.voff[j - 4] + (uint32_t)job.k0 : kOutOfRange,
+              job.rb);
 }
 
-// One half step: 16 MFMAs on the current fragments, with the 16 LDS reads of
-// the next half step's fragments placed between them.
+// One half step: 16 MFMAs on the current fragments.  Between them go the
+// 16 LDS reads of the next half step's fragments and, after every second
+// MFMA, one DMA instruction of the job, so that neither the LDS reads nor
+// the DMA issue (which can stall while the address FIFO is full) hold up
+// the MFMA stream.
 template <int FA, int FB, bool FIRST>
 __device__ inline void half_step(v16f (&acc)[4][4], const v8i (&ca)[4], const v8i (&cb)[4], v8i (&na)[4],
-                                 v8i (&nb)[4], const uint8_t* la, const uint8_t* lb, int wm, int wn)
+                                 v8i (&nb)[4], const uint8_t* la, const uint8_t* lb, int wm, int wn,
+                                 const DmaJob& job, const Offsets& oa, const Offsets& ob, int k)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (FIRST)
-                acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], v16f{});
-            else
-                acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], acc[i][j]);
-        }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) nb[j] = frag32(lb, wn + 32 * j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) na[i] = frag32(la, wm + 32 * i);
-#pragma unroll
     for (int s = 0; s < 16; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one ds_read
+        const int i = s >> 2, j = s & 3;
+        if constexpr (FIRST)
+            acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], v16f{});
+        else
+            acc[i][j] = mfma32<FA, FB>(ca[i], cb[j], acc[i][j]);
+        // reads: B fragments first (s = 0..7), then A
+        const int f = s >> 1;
+        const int row0 = f < 4 ? wn + 32 * f : wm + 32 * (f - 4);
+        const uint8_t* base = f < 4 ? lb : la;
+        const int l = threadIdx.x & 63;
+        const int r = row0 + (l & 31);
+        const int c = (l >> 5) * 2 + (s & 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(base + r * KH + swz4(r, c) * 16);
+        v8i& dst = f < 4 ? nb[f] : na[f - 4];
+        if ((s & 1) == 0) {
+            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+        } else {
+            dst[4] = v.x; dst[5] = v.y; dst[6] = v.z; dst[7] = v.w;
+            dma_one(job, oa, ob, f, k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     // Pin the MFMAs to this half step: an MFMA touches no memory, so without
     // a use here the compiler may sink it past the next half step's wait and
@@ -257,22 +284,28 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
     Cursor c = d;
     if (!c.valid) return;
 
-    auto issue = [&](int stage) -> int {
-        if (!d.valid) return 0;
+    const int wave_slot = wave * 4 * 1024;
+    auto make_job = [&](int stage) -> DmaJob {
+        DmaJob job;
+        const bool v = d.valid;
         const Item& it = d.it;
-        const v4u ra = make_rsrc(p.a + (int64_t)it.m0 * p.lda, (uint32_t)(min(BM, p.m - it.m0) * p.lda));
-        const v4u rb = make_rsrc(p.b + (int64_t)it.n0 * p.ldb, (uint32_t)(min(BN, p.n - it.n0) * p.ldb));
-        dma_half(oa, ra, lds_a0 + stage * kStageBytes, d.h * KH, p.k);
-        dma_half(ob, rb, lds_b0 + stage * kStageBytes, d.h * KH, p.k);
-        cursor_next(p, d, xcd, slot);
-        return kDmaPerHalf;
+        job.ra = make_rsrc(p.a + (int64_t)it.m0 * p.lda, v ? (uint32_t)(min(BM, p.m - it.m0) * p.lda) : 0u);
+        job.rb = make_rsrc(p.b + (int64_t)it.n0 * p.ldb, v ? (uint32_t)(min(BN, p.n - it.n0) * p.ldb) : 0u);
+        job.lds_a = lds_a0 + stage * kStageBytes + wave_slot;
+        job.lds_b = lds_b0 + stage * kStageBytes + wave_slot;
+        job.k0 = d.h * KH;
+        if (v) cursor_next(p, d, xcd, slot);
+        return job;
     };
 
     // prologue: half steps 0..3 into stages 0..3, then the fragments of half 0
-    issue(0);
-    const int dq1 = issue(1);
-    int dq2 = issue(2), dq3 = issue(3);   // DMA counts of half steps t+2, t+3
-    wait_vmcnt(dq1 + dq2 + dq3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const DmaJob job = make_job(q);
+#pragma unroll
+        for (int j = 0; j < kDmaPerHalf; ++j) dma_one(job, oa, ob, j, p.k);
+    }
+    wait_vmcnt(3 * kDmaPerHalf);
     barrier_only();
     v8i ra0[4], rb0[4], ra1[4], rb1[4];
 #pragma unroll
@@ -286,22 +319,22 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
     int t = 0;                     // half-step index in this workgroup's stream
 
     // Half step t: MFMAs on (cur_a, cur_b), fragments of half step t+1 read
-    // into (nxt_a, nxt_b).  Issue order per half step: DMA(t+4), then (after
-    // a tile's last half step) the epilogue's stores, so DMA(t+1), issued in
-    // half step t-3, is complete once at most the stores of t-3..t-1 and
-    // DMA(t+2), DMA(t+3) are pending.
+    // into (nxt_a, nxt_b), DMA of half step t+4 into the stage half step t
+    // has released.  Every half step issues its 8 DMA instructions, then
+    // (after a tile's last half step) the epilogue's stores, so DMA(t+1),
+    // issued in half step t-3, is complete once at most the stores of
+    // t-3..t-1 and the 16 DMA instructions of t+2, t+3 are pending.
     auto half = [&](auto first, const v8i (&cur_a)[4], const v8i (&cur_b)[4], v8i (&nxt_a)[4], v8i (&nxt_b)[4]) {
-        wait_vmcnt(dq2 + dq3 + s3 + s2 + s1);
+        const DmaJob job = make_job(t & 3);
+        wait_vmcnt(2 * kDmaPerHalf + s3 + s2 + s1);
         // every wave has read its half-t fragments out of stage t%4, and half
         // t+1's data is in stage (t+1)%4
         barrier_lds();
-        const int dq4 = issue(t & 3);
         // (after the stream's last half step this reads a stale stage: harmless)
         const uint8_t* la = s_lds_a + ((t + 1) & 3) * kStageBytes;
         const uint8_t* lb = s_lds_b + ((t + 1) & 3) * kStageBytes;
-        half_step<FA, FB, decltype(first)::value>(acc, cur_a, cur_b, nxt_a, nxt_b, la, lb, wm, wn);
-        dq2 = dq3;
-        dq3 = dq4;
+        half_step<FA, FB, decltype(first)::value>(acc, cur_a, cur_b, nxt_a, nxt_b, la, lb, wm, wn, job, oa, ob,
+                                                  p.k);
         s3 = s2;
         s2 = s1;
         s1 = 0;
