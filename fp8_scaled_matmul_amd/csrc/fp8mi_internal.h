@@ -11,7 +11,7 @@
 namespace fp8mi {
 
 // Number of per-workgroup partial maxima the per-tensor amax pass writes.
-constexpr int kAmaxPartials = 1024;
+constexpr int kAmaxPartials = 2048;
 constexpr size_t kAmaxWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
 
 // Quantizer launch description (all pointers device pointers).

@@ -23,6 +23,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Fast amax of bf16 data: the |x| bit patterns of two elements per word,
+// maxed two at a time (v_pk_max_u16).  Patterns of finite values order like
+// their magnitudes; a result >= 0x7F80 means some element was Inf or NaN, and
+// the caller then redoes the exact, flag-carrying merge (key_merge).
+__device__ inline us2 pkmax8(us2 m, const uint4& w)
+{
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w.x & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w.y & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w.z & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w.w & 0x7FFF7FFFu));
+    return m;
+}
+// The packed max as an fp32 |x| bit pattern (>= 0x7F800000: non-finite seen).
+__device__ inline uint32_t pk_raw(us2 m) { return (uint32_t)(m.x > m.y ? m.x : m.y) << 16; }
+constexpr uint32_t kRawNonFinite = 0x7F800000u;
+
 // ------------------------------------------------------------------ loads
 // 8 consecutive elements as fp32 plus their amax key.  DT 0 = bf16, 1 = fp32.
 template <int DT>
@@ -120,32 +138,91 @@ __device__ inline uint32_t block_key_merge(uint32_t k)
 }
 
 // ------------------------------------------------------------------ amax
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes read once: a nontemporal load (the data is not reused).
+__device__ inline uint4 ld_stream(const void* p)
+{
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Each workgroup reads a contiguous range of each row it is given (DRAM
+// pages stay open: measured faster than a grid-strided interleave).
+template <int DT, bool EXACT>
+__device__ inline uint32_t amax_share(const void* x, int64_t rows, int64_t cols, int64_t ld, int vec)
+{
+    uint32_t key = 0;           // EXACT: merged key; else fp32 |x| bits max (fp32 input)
+    us2 pk = us2{0, 0};         // bf16 fast path
+    const int64_t nvec = vec ? cols / 8 : 0;
+    const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = min(nvec, b0 + per);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const int64_t base = r * ld;
+        int64_t i = b0 + threadIdx.x;
+        if constexpr (DT == 0 && !EXACT) {
+            const uint16_t* xb = static_cast<const uint16_t*>(x) + base;
+            for (; i + 7 * kThreads < b1; i += 8 * kThreads) {
+                uint4 w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) w[u] = ld_stream(xb + (i + u * kThreads) * 8);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) pk = pkmax8(pk, w[u]);
+            }
+            for (; i < b1; i += kThreads) pk = pkmax8(pk, ld_stream(xb + i * 8));
+            for (int64_t c = nvec * 8 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride) {
+                const uint32_t h = xb[c] & 0x7FFFu;
+                pk.x = pk.x > h ? pk.x : (unsigned short)h;
+            }
+        } else if constexpr (DT == 1 && !EXACT) {
+            const uint32_t* xb = static_cast<const uint32_t*>(x) + base;
+            for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+                uint4 w[8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    w[2 * u] = ld_stream(xb + (i + u * kThreads) * 8);
+                    w[2 * u + 1] = ld_stream(xb + (i + u * kThreads) * 8 + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    key = max(max(max(key, w[u].x & 0x7FFFFFFFu), max(w[u].y & 0x7FFFFFFFu, w[u].z & 0x7FFFFFFFu)),
+                              w[u].w & 0x7FFFFFFFu);
+            }
+            for (; i < b1; i += kThreads) {
+                const uint4 a = ld_stream(xb + i * 8);
+                const uint4 b = ld_stream(xb + i * 8 + 4);
+                key = max(max(max(key, a.x & 0x7FFFFFFFu), max(a.y & 0x7FFFFFFFu, a.z & 0x7FFFFFFFu)),
+                          a.w & 0x7FFFFFFFu);
+                key = max(max(max(key, b.x & 0x7FFFFFFFu), max(b.y & 0x7FFFFFFFu, b.z & 0x7FFFFFFFu)),
+                          b.w & 0x7FFFFFFFu);
+            }
+            for (int64_t c = nvec * 8 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride)
+                key = max(key, xb[c] & 0x7FFFFFFFu);
+        } else {
+            for (; i < b1; i += kThreads) {
+                float v[8];
+                load8<DT>(x, base + i * 8, v, key);
+            }
+            for (int64_t c = nvec * 8 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride)
+                (void)load1<DT>(x, base + c, key);
+        }
+    }
+    if constexpr (DT == 0 && !EXACT) key = pk_raw(pk);
+    return key;
+}
+
 // Pass 1 of per-tensor scaling: each workgroup reduces a grid-strided share
 // of the [rows, cols] tensor (a contiguous tensor arrives as one long row) to
 // one key.  vec: rows start 16-byte aligned, so 8-element vectors are used.
+// A thread whose share holds an Inf or NaN redoes it with the exact merge.
 template <int DT>
 __global__ void __launch_bounds__(kThreads) k_amax_partials(const void* x, int64_t rows, int64_t cols,
                                                             int64_t ld, int vec, uint32_t* partials)
 {
-    uint32_t key = 0;
-    const int64_t nvec = vec ? cols / 8 : 0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        const int64_t base = r * ld;
-        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-        // four vectors in flight per thread
-        for (; i + 3 * stride < nvec; i += 4 * stride) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) load8<DT>(x, base + (i + u * stride) * 8, v, key);
-        }
-        for (; i < nvec; i += stride) {
-            float v[8];
-            load8<DT>(x, base + i * 8, v, key);
-        }
-        for (int64_t c = nvec * 8 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride)
-            (void)load1<DT>(x, base + c, key);
-    }
+    uint32_t key = amax_share<DT, false>(x, rows, cols, ld, vec);
+    if (key >= kRawNonFinite) key = amax_share<DT, true>(x, rows, cols, ld, vec);
     key = block_key_merge(key);
     if (threadIdx.x == 0) partials[blockIdx.y * gridDim.x + blockIdx.x] = key;
 }
@@ -243,7 +320,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
                                                       int64_t ld, int vec, float* scale,
                                                       const uint32_t* partials, int np, uint8_t* q,
                                                       int64_t ldq, uint8_t* qt, int64_t ldqt,
-                                                      fp8_counters* ctr)
+                                                      fp8_counters* ctr, int only_partial)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTilePitch];
     const int t = threadIdx.x;
@@ -271,6 +348,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
         const int64_t r0 = (tid / tiles_c) * kTile;
         const int64_t c0 = (tid % tiles_c) * kTile;
         const bool full = vec && r0 + kTile <= rows && c0 + kTile <= cols;
+        if (only_partial && r0 + kTile <= rows && c0 + kTile <= cols) continue;   // done by k_tile128_bf16
         float xv[8][8];
         uint32_t key = 0;
         if (full) {
@@ -370,6 +448,293 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
         }
     }
     if constexpr (!AMAX_ONLY) flush_counters(ctr, sat, und, nan);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its outstanding global loads (__syncthreads() also drains vmcnt, which
+// would wait for the prefetched next tile).
+__device__ inline void barrier_lds_only()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ inline uint32_t block_key_merge_lds(uint32_t k)
+{
+    __shared__ uint32_t sh[kThreads / 64];
+    k = wave_key_merge(k);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = k;
+    barrier_lds_only();
+    k = sh[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) k = key_merge(k, sh[w]);
+    barrier_lds_only();
+    return k;
+}
+
+// ------------------------------------------------------------------ 128x128 tiles, bf16 fast path
+// Full 128x128 tiles of a 16-byte aligned bf16 tensor.  Thread t owns the
+// 8x8 block of rows 8 (t/16) + i, columns 8 (t%16) + j (eight 16-byte row
+// loads; 16 lanes cover a 256-byte row segment).  The next tile's loads are
+// issued before the current tile is processed.  Codes leave row-major as 8
+// bytes per row; for the transposed copy the thread transposes its 8x8 byte
+// block in registers (v_perm_b32) and writes 8 bytes per column to an LDS
+// tile of 128 output rows x 128 bytes, whose 8-byte chunks are swizzled so
+// that both the writes and the 16-byte row reads are free of bank
+// conflicts; each thread then stores 64 bytes of one output row.
+// SCALE_MODE as in k_tile128.  Edge tiles are left to k_tile128.
+__device__ inline int tswz(int c) { return ((c >> 3) & 15) ^ ((c & 7) << 1); }
+
+template <int FMT, int SCALE_MODE>
+__global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, int64_t rows, int64_t cols,
+                                                           int64_t ld, float* scale, const uint32_t* partials,
+                                                           int np, uint8_t* q, int64_t ldq, uint8_t* qt,
+                                                           int64_t ldqt, fp8_counters* ctr)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tt[kTile * kTile];
+    const int t = threadIdx.x;
+    const int g = t >> 4, k = t & 15;
+    const int64_t tiles_c = cols / kTile;       // full tiles only
+    const int64_t ntiles = (rows / kTile) * tiles_c;
+    const int64_t tiles_c_all = (cols + kTile - 1) / kTile;
+
+    float s_tensor = 1.0f;
+    bool special_tensor = true;
+    if constexpr (SCALE_MODE == 0) {
+        if (partials) {
+            const uint32_t kk = reduce_partials(partials, np);
+            special_tensor = key_special(kk);
+            s_tensor = scale_from_amax<FMT>(key_amax(kk));
+            if (blockIdx.x == 0 && t == 0) scale[0] = s_tensor;
+        } else {
+            s_tensor = scale[0];
+        }
+    }
+    uint32_t sat = 0, und = 0, nan = 0;
+
+    auto load = [&](int64_t id, uint4 (&w)[8]) {
+        const int64_t r0 = (id / tiles_c) * kTile, c0 = (id % tiles_c) * kTile;
+        const uint16_t* src = x + (r0 + 8 * g) * ld + c0 + 8 * k;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = ld_stream(src + i * ld);
+    };
+
+    // a contiguous range of tiles (row-major tile order) per workgroup; the
+    // loop is unrolled by two so the prefetch buffers alternate statically
+    const int64_t per = (ntiles + gridDim.x - 1) / gridDim.x;
+    const int64_t id0 = (int64_t)blockIdx.x * per;
+    const int64_t id1 = min(ntiles, id0 + per);
+
+    auto process = [&](const uint4 (&cur)[8], int64_t id) {
+        const int64_t r0 = (id / tiles_c) * kTile, c0 = (id % tiles_c) * kTile;
+
+        float s;
+        bool fast;
+        if constexpr (SCALE_MODE == 0) {
+            s = s_tensor;
+            fast = partials && !special_tensor && s >= kCorrectedQuotMinScale;
+        } else if constexpr (SCALE_MODE == 1) {
+            us2 m = us2{0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = pkmax8(m, cur[i]);
+            uint32_t key = block_key_merge_lds(pk_raw(m));
+            if (key >= kRawNonFinite) {
+                // an Inf or NaN in the block: the exact merge (finite amax + flag)
+                // (rare: the rows are read again rather than indexed in
+                // registers, which would move the tile to scratch memory)
+                uint32_t e = 0;
+                const uint16_t* src = x + (r0 + 8 * g) * ld + c0 + 8 * k;
+#pragma unroll 1
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(src + i * ld);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
+                        e = key_merge(e, absbits_bf16(ws[h] >> 16));
+                    }
+                }
+                key = block_key_merge_lds(e);
+            }
+            s = scale_from_amax<FMT>(key_amax(key));
+            if (t == 0) scale[(r0 / kTile) * tiles_c_all + c0 / kTile] = s;
+            fast = !key_special(key) && s >= kCorrectedQuotMinScale;
+        } else {
+            s = scale[(r0 / kTile) * tiles_c_all + c0 / kTile];
+            fast = false;
+        }
+
+        uint8_t* qrow = q + (r0 + 8 * g) * ldq + c0 + 8 * k;
+        if (fast) {
+            const float r = 1.0f / s;
+            // rows 4 rb .. 4 rb + 3: cast, store, transpose their 4x8 bytes
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                uint2 code[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 w = cur[4 * rb + i];
+                    float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                    code[i] = cast8<FMT, true>(v, s, r, sat, und, nan);
+                    *reinterpret_cast<uint2*>(qrow + (4 * rb + i) * ldq) = code[i];
+                    // one row at a time: keeps the quotient temporaries of the
+                    // other rows from being live at once
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (qt) {
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {      // columns 4 half .. +3
+                        const uint32_t a = half ? code[0].y : code[0].x;
+                        const uint32_t b = half ? code[1].y : code[1].x;
+                        const uint32_t c = half ? code[2].y : code[2].x;
+                        const uint32_t d = half ? code[3].y : code[3].x;
+                        const uint32_t x0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+                        const uint32_t x1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+                        const uint32_t y0 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+                        const uint32_t y1 = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+                        const uint32_t col[4] = {__builtin_amdgcn_perm(y0, x0, 0x05040100u),
+                                                 __builtin_amdgcn_perm(y0, x0, 0x07060302u),
+                                                 __builtin_amdgcn_perm(y1, x1, 0x05040100u),
+                                                 __builtin_amdgcn_perm(y1, x1, 0x07060302u)};
+                        // output row cc = 8 k + 4 half + j, logical chunk g, bytes 4 rb .. +3
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int cc = 8 * k + 4 * half + j;
+                            *reinterpret_cast<uint32_t*>(&tt[cc * kTile + 8 * (g ^ tswz(cc)) + 4 * rb]) = col[j];
+                        }
+                    }
+                }
+            }
+        } else {
+            // general quotients (IEEE division, all counters), one row at a
+            // time; the rows are read again (indexing the registers by a loop
+            // variable would move the tile to scratch memory)
+            const uint16_t* src = x + (r0 + 8 * g) * ld + c0 + 8 * k;
+#pragma unroll 1
+            for (int i = 0; i < 8; ++i) {
+                const uint4 w = *reinterpret_cast<const uint4*>(src + i * ld);
+                float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                              bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                const uint2 code = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+                *reinterpret_cast<uint2*>(qrow + i * ldq) = code;
+                if (qt) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int cc = 8 * k + j;
+                        tt[cc * kTile + 8 * (g ^ tswz(cc)) + i] = (uint8_t)((j < 4 ? code.x : code.y) >> (8 * (j & 3)));
+                    }
+                }
+            }
+        }
+
+        if (qt) {
+            barrier_lds_only();
+            const int c = t & 127, hh = t >> 7;
+            const int sw = tswz(c);
+            uint8_t* dst = qt + (c0 + c) * ldqt + r0 + 64 * hh;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int p0 = (8 * hh + 2 * m) ^ sw;           // physical chunk of logical 8hh+2m
+                uint4 v = *reinterpret_cast<const uint4*>(&tt[c * kTile + 8 * (p0 & ~1)]);
+                if (p0 & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+                *reinterpret_cast<uint4*>(dst + 16 * m) = v;
+            }
+            barrier_lds_only();
+        }
+    };
+
+    uint4 bufa[8], bufb[8];
+    int64_t id = id0;
+    if (id < id1) load(id, bufa);
+    while (id < id1) {
+        if (id + 1 < id1) load(id + 1, bufb);
+        process(bufa, id);
+        if (++id >= id1) break;
+        if (id + 1 < id1) load(id + 1, bufa);
+        process(bufb, id);
+        ++id;
+    }
+    flush_counters(ctr, sat, und, nan);
+}
+
+// ------------------------------------------------------------------ 1x128 row tiles, bf16 fast path
+// Full tiles of a 16-byte aligned bf16 tensor, scale from each tile's amax.
+// 16 lanes per tile and 4 tiles per group and iteration, all loads first.
+// The 16-lane amax is a packed max of |x| patterns (exact merge only for a
+// tile holding Inf or NaN); lane u of each group then divides for tile u and
+// the scales and reciprocals are shuffled back, one pair of divisions per
+// lane for 4 tiles.
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, int64_t ld, float* scale,
+                                                            uint8_t* q, int64_t ldq, fp8_counters* ctr,
+                                                            uint32_t ntiles, FastDiv tiles_per_row,
+                                                            uint32_t scale_ld)
+{
+    constexpr int U = 4;
+    constexpr uint32_t kChunk = (kThreads / 16) * U;     // tiles per workgroup and iteration
+    const int lane = threadIdx.x & 15;
+    const uint32_t gi = threadIdx.x >> 4;                // group in the workgroup
+    uint32_t sat = 0, und = 0, nan = 0;
+    // a contiguous range of tiles per workgroup, walked in chunks of 64
+    // consecutive tiles (group gi takes tiles 4 gi .. 4 gi + 3 of a chunk):
+    // consecutive tiles of a row are consecutive in memory
+    const uint32_t per = ((ntiles + gridDim.x - 1) / gridDim.x + kChunk - 1) / kChunk * kChunk;
+    const uint32_t w0 = blockIdx.x * per;
+    const uint32_t g1 = min(ntiles, w0 + per);
+    for (uint32_t t0 = w0 + gi * U; t0 < g1; t0 += kChunk) {
+        uint4 w[U];
+        uint32_t row[U], tc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t tile = t0 + u;
+            const uint32_t tl = tile < g1 ? tile : g1 - 1;   // clamp: loads stay in range
+            row[u] = tiles_per_row.div(tl);
+            tc[u] = tl - row[u] * tiles_per_row.d;
+            w[u] = ld_stream(x + (int64_t)row[u] * ld + tc[u] * 128 + lane * 8);
+        }
+        uint32_t key[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint32_t k2 = pk_raw(pkmax8(us2{0, 0}, w[u]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) k2 = max(k2, (uint32_t)__shfl_xor(k2, off, 16));
+            if (k2 >= kRawNonFinite) {
+                const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                uint32_t e = 0;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
+                    e = key_merge(e, absbits_bf16(ws[h] >> 16));
+                }
+#pragma unroll
+                for (int off = 8; off >= 1; off >>= 1) e = key_merge(e, __shfl_xor(e, off, 16));
+                k2 = e;
+            }
+            key[u] = k2;
+        }
+        // lane u (u < U) of the group derives the scale of tile u
+        const uint32_t mykey = lane == 0 ? key[0] : lane == 1 ? key[1] : lane == 2 ? key[2] : key[3];
+        const float my_s = scale_from_amax<FMT>(key_amax(mykey));
+        const float my_r = 1.0f / my_s;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t tile = t0 + u;
+            const float s = __shfl(my_s, u, 16);
+            const float r = __shfl(my_r, u, 16);
+            if (tile >= g1) continue;
+            if (lane == 0) scale[(int64_t)row[u] * scale_ld + tc[u]] = s;
+            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+            float v[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[2 * h] = bf16_lo(ws[h]);
+                v[2 * h + 1] = bf16_hi(ws[h]);
+            }
+            const bool fast = !key_special(key[u]) && s >= kCorrectedQuotMinScale;
+            const uint2 o = fast ? cast8<FMT, true>(v, s, r, sat, und, nan) : cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+            *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + tc[u] * 128 + lane * 8) = o;
+        }
+    }
+    flush_counters(ctr, sat, und, nan);
 }
 
 // ------------------------------------------------------------------ 1x128 row tiles
@@ -480,6 +845,30 @@ dim3 stream_grid(int64_t rows, int64_t cols, int per_thread, int max_wg)
     return dim3((unsigned)gx, (unsigned)gy, 1);
 }
 
+// 128x128 tiles: full tiles of an aligned bf16 tensor go to k_tile128_bf16,
+// the rest (edge tiles, fp32 input, unaligned layouts) to k_tile128.
+template <int FMT, int DT, int SCALE_MODE>
+hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int np, hipStream_t stream)
+{
+    const int64_t rows = a.rows, cols = a.cols;
+    const int64_t nt = cdiv(rows, kTile) * cdiv(cols, kTile);
+    const int64_t nfull = (rows / kTile) * (cols / kTile);
+    int only_partial = 0;
+    if (DT == 0 && vec && nfull > 0) {
+        const int grid = (int)std::min<int64_t>(nfull, (int64_t)num_cus() * 4);
+        hipLaunchKernelGGL((k_tile128_bf16<FMT, SCALE_MODE>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, parts, np, a.q, a.ldq,
+                           a.qt, a.ldqt, a.ctr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || nfull == nt) return e;
+        only_partial = 1;
+    }
+    const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
+    hipLaunchKernelGGL((k_tile128<FMT, DT, SCALE_MODE, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
+                       cols, a.ld, vec, a.scale, parts, np, a.q, a.ldq, a.qt, a.ldqt, a.ctr, only_partial);
+    return hipGetLastError();
+}
+
 template <int FMT, int DT>
 hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
 {
@@ -503,10 +892,7 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
         if (a.qt) {
             const int vec = aligned16(a.x) && aligned16(a.q) && aligned16(a.qt) && (a.ld * eb) % 16 == 0 &&
                             a.ldq % 8 == 0 && a.ldqt % 16 == 0;
-            const int64_t nt = cdiv(rows, kTile) * cdiv(cols, kTile);
-            const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
-            hipLaunchKernelGGL((k_tile128<FMT, DT, 0, false>), dim3(grid), dim3(kThreads), 0, stream, a.x,
-                               rows, cols, a.ld, vec, a.scale, parts, np, a.q, a.ldq, a.qt, a.ldqt, a.ctr);
+            return launch_tiles<FMT, DT, 0>(a, vec, parts, np, stream);
         } else {
             int64_t r = rows, c = cols, ld = a.ld, ldq = a.ldq;
             flatten(r, c, ld, &ldq);
@@ -521,20 +907,20 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
     if (a.gran == FP8_BLOCK_128x128) {
         const int vec = aligned16(a.x) && aligned16(a.q) && (!a.qt || aligned16(a.qt)) && (a.ld * eb) % 16 == 0 &&
                         a.ldq % 8 == 0 && (!a.qt || a.ldqt % 16 == 0);
-        const int64_t nt = cdiv(rows, kTile) * cdiv(cols, kTile);
-        const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
-        if (a.mode == FP8_SCALE_FROM_AMAX)
-            hipLaunchKernelGGL((k_tile128<FMT, DT, 1, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
-                               cols, a.ld, vec, a.scale, nullptr, 0, a.q, a.ldq, a.qt, a.ldqt, a.ctr);
-        else
-            hipLaunchKernelGGL((k_tile128<FMT, DT, 2, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
-                               cols, a.ld, vec, a.scale, nullptr, 0, a.q, a.ldq, a.qt, a.ldqt, a.ctr);
-        return hipGetLastError();
+        if (a.mode == FP8_SCALE_FROM_AMAX) return launch_tiles<FMT, DT, 1>(a, vec, nullptr, 0, stream);
+        return launch_tiles<FMT, DT, 2>(a, vec, nullptr, 0, stream);
     }
     // ROW_1x128
     const int64_t tpr = cdiv(cols, 128);
     const int64_t ntiles = rows * tpr;
     const int vec = aligned16(a.x) && (a.ld * eb) % 16 == 0 && a.ldq % 8 == 0 && aligned16(a.q);
+    if (DT == 0 && vec && cols % 128 == 0 && a.mode == FP8_SCALE_FROM_AMAX) {
+        const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16 * 4), (int64_t)num_cus() * 8);
+        hipLaunchKernelGGL(k_row1x128_bf16<FMT>, dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(a.x), a.ld, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles,
+                           FastDiv((uint32_t)tpr), (uint32_t)tpr);
+        return hipGetLastError();
+    }
     const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16), (int64_t)num_cus() * 16);
     if (a.mode == FP8_SCALE_FROM_AMAX)
         hipLaunchKernelGGL((k_row1x128<FMT, DT, false, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
@@ -593,10 +979,10 @@ hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t c
         const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
         if (dtype == FP8_IN_BF16)
             hipLaunchKernelGGL((k_tile128<0, 0, 1, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, ld,
-                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr);
+                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
         else
             hipLaunchKernelGGL((k_tile128<0, 1, 1, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, ld,
-                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr);
+                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
         return hipGetLastError();
     }
     const int64_t tpr = cdiv(cols, 128);

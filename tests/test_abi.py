@@ -47,10 +47,10 @@ def test_abi_version_and_strings(L):
 
 
 def test_workspace_sizes(L):
-    assert L.fp8_quantize_workspace_size(10, 10, fm.TENSOR, fm.FROM_AMAX) == 4096
+    assert L.fp8_quantize_workspace_size(10, 10, fm.TENSOR, fm.FROM_AMAX) == 8192
     assert L.fp8_quantize_workspace_size(10, 10, fm.TENSOR, fm.GIVEN) == 0
     assert L.fp8_quantize_workspace_size(10, 10, fm.ROW_1x128, fm.FROM_AMAX) == 0
-    assert L.fp8_amax_workspace_size(10, 10, fm.TENSOR) == 4096
+    assert L.fp8_amax_workspace_size(10, 10, fm.TENSOR) == 8192
     # dW of the speedrun backward: few output tiles, long K -> split-K workspace
     assert L.fp8_scaled_mm_workspace_size(3072, 768, 65536, 0, 0) > 0
     assert L.fp8_scaled_mm_workspace_size(65536, 3072, 768, 0, 0) == 0
@@ -83,7 +83,7 @@ BAD = 0x1000  # a non-null address never dereferenced: every call below fails va
 def test_quantize_rejects_before_device(L, args, code):
     a = dict(x=BAD, dtype=fm.BF16, rows=64, cols=32, ld=32, fmt=fm.E4M3, gran=fm.TENSOR,
              mode=fm.FROM_AMAX, scale=BAD, q=BAD, ldq=32, q_t=None, ldq_t=0, ctr=None,
-             ws=BAD, wsb=4096)
+             ws=BAD, wsb=8192)
     a.update(args)
     rc = fm.fp8_quantize(a["x"], a["dtype"], a["rows"], a["cols"], a["ld"], a["fmt"], a["gran"],
                          a["mode"], a["scale"], a["q"], a["ldq"], a["q_t"], a["ldq_t"], a["ctr"],
