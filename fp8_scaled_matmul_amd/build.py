@@ -28,12 +28,17 @@ FLAGS = [
 ]
 
 
+# Per-file extras.  The block-scaled GEMM promotes each MFMA result on the
+# VALU: MFMA results written straight to VGPRs save a copy out of AGPRs.
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, src + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

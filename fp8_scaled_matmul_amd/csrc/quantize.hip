@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(kThreads) k_cast_tensor(const void* x, int64_t
     } else {
         cast_stream<FMT, DT, false>(x, rows, cols, ld, vec, q, ldq, s, 0.0f, sat, und, nan);
     }
-    flush_counters(ctr, sat, und, nan);
+    flush_counters_block(ctr, sat, und, nan);
 }
 
 // ------------------------------------------------------------------ 128x128 tiles
@@ -447,7 +447,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
             __syncthreads();
         }
     }
-    if constexpr (!AMAX_ONLY) flush_counters(ctr, sat, und, nan);
+    if constexpr (!AMAX_ONLY) flush_counters_block(ctr, sat, und, nan);
 }
 
 // Workgroup barrier that waits only for this wave's LDS operations, not for
@@ -653,7 +653,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
         process(bufb, id);
         ++id;
     }
-    flush_counters(ctr, sat, und, nan);
+    flush_counters_block(ctr, sat, und, nan);
 }
 
 // ------------------------------------------------------------------ 1x128 row tiles, bf16 fast path
@@ -734,7 +734,7 @@ __global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, i
             *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + tc[u] * 128 + lane * 8) = o;
         }
     }
-    flush_counters(ctr, sat, und, nan);
+    flush_counters_block(ctr, sat, und, nan);
 }
 
 // ------------------------------------------------------------------ 1x128 row tiles
@@ -793,7 +793,7 @@ __global__ void __launch_bounds__(kThreads) k_row1x128(const void* x, int64_t ro
                                                          : cast1<FMT, false>(xv[j], s, 0.0f, sat, und, nan);
         }
     }
-    if constexpr (!AMAX_ONLY) flush_counters(ctr, sat, und, nan);
+    if constexpr (!AMAX_ONLY) flush_counters_block(ctr, sat, und, nan);
 }
 
 __global__ void k_counters_reset(fp8_counters* ctr)
@@ -915,7 +915,7 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
     const int64_t ntiles = rows * tpr;
     const int vec = aligned16(a.x) && (a.ld * eb) % 16 == 0 && a.ldq % 8 == 0 && aligned16(a.q);
     if (DT == 0 && vec && cols % 128 == 0 && a.mode == FP8_SCALE_FROM_AMAX) {
-        const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16 * 4), (int64_t)num_cus() * 8);
+        const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16 * 4), (int64_t)num_cus() * 4);
         hipLaunchKernelGGL(k_row1x128_bf16<FMT>, dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.x), a.ld, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles,
                            FastDiv((uint32_t)tpr), (uint32_t)tpr);

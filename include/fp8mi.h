@@ -117,7 +117,10 @@ fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, 
  *   q_t    optional out (NULL = none): the byte transpose [cols, rows],
  *          leading dimension ldq_t >= rows.  TENSOR and BLOCK_128x128 only
  *          (a 1x128 row tile does not transpose into a 1x128 row tile:
- *          FP8_ERR_UNSUPPORTED_SHAPE).
+ *          FP8_ERR_UNSUPPORTED_SHAPE).  When rows is a multiple of 64 KiB
+ *          (e.g. 65536 tokens), pad ldq_t (by 256, say): rows that lie a
+ *          multiple of 64 KiB apart share HBM channels, which slows both
+ *          this write and a GEMM that reads q_t as an operand.
  *   ctr    optional counters (NULL = none).
  *   workspace  TENSOR + FROM_AMAX needs fp8_quantize_workspace_size() bytes;
  *          the other modes need none.
