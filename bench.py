@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=32768)
+    p.add_argument("--cpu-sample-rows", type=int, default=65536)
     return p.parse_args()
 
 
@@ -220,26 +220,36 @@ def main():
 
 
 def cpu_baseline(sample_rows: int, stage_ms: dict):
-    """The oracle, as it stands, on a bounded sample of the same work: a
-    row sample of the forward up-projection (quantize X rows with the oracle,
-    then its fp64 GEMM against all of W).  Reported in the metric's unit."""
+    """The oracle, as it stands, on a bounded sample of the same work: the
+    per-tensor part of the step (oracle quantization of X, W and dY with their
+    transposed copies, then its fp64 GEMMs forward, dX and dW) on the first
+    `sample_rows` token rows (all 65536 by default).  Reported in the
+    metric's unit (GEMM TFLOP/s)."""
     import numpy as np
 
     import oracle
     import synth
 
-    x = synth.normal_bf16(3, 0, (TOK, D), 1.0)[:sample_rows]
+    rows = min(sample_rows, TOK)
+    x = synth.normal_bf16(3, 0, (TOK, D), 1.0)[:rows]
     w = synth.normal_bf16(3, 1, (F, D), 0.02)
+    dy = synth.normal_bf16(5, 0, (TOK, F), 1e-3)[:rows]
     t0 = time.time()
-    xq, _, xs, _ = oracle.quantize(x, oracle.E4M3)
-    wq, _, ws, _ = oracle.quantize(w, oracle.E4M3)
-    y = oracle.gemm(xq, 0, xs, 0, wq, 0, ws, 0)
-    dt = time.time() - t0
-    flops = 2.0 * sample_rows * F * D
+    xq, xqt, xs, _ = oracle.quantize(x, oracle.E4M3, want_t=True)
+    wq, wqt, ws, _ = oracle.quantize(w, oracle.E4M3, want_t=True)
+    dyq, dyqt, dys, _ = oracle.quantize(dy, oracle.E5M2, want_t=True)
+    y = oracle.gemm(xq, oracle.E4M3, xs, oracle.TENSOR, wq, oracle.E4M3, ws, oracle.TENSOR)
     del y
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"forward up-projection on {sample_rows} of {TOK} token rows: oracle quantize of X rows "
-                      f"and W, then fp64 GEMM {sample_rows}x{F}x{D}; {dt:.1f} s",
+    dx = oracle.gemm(dyq, oracle.E5M2, dys, oracle.TENSOR, wqt, oracle.E4M3, ws, oracle.TENSOR)
+    del dx
+    dw = oracle.gemm(dyqt, oracle.E5M2, dys, oracle.TENSOR, xqt, oracle.E4M3, xs, oracle.TENSOR)
+    del dw
+    dt = time.time() - t0
+    flops = 3 * 2.0 * rows * F * D
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"per-tensor up-projection step on {rows} of {TOK} token rows: oracle quantization of X, W, "
+                      f"dY (+ transposed copies), fp64 GEMMs fwd {rows}x{F}x{D}, dX {rows}x{D}x{F}, "
+                      f"dW {F}x{D}x{rows}; {dt:.1f} s",
             "seconds": round(dt, 2)}
 
 

@@ -224,17 +224,25 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af[i], bf[j], acc[i][j]);
         } else {
+            // Each MFMA covers one 128-deep K block of a 16x16 tile; its 4
+            // results are promoted kLag MFMAs later, so the FMAs find them
+            // written without the wait states an immediate read would need.
+            constexpr int kLag = 3;
+            v4f part[kLag + 1];
+            v4f cf[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float c0 = sa4[i].x * sbv, c1 = sa4[i].y * sbv, c2 = sa4[i].z * sbv, c3 = sa4[i].w * sbv;
+            for (int i = 0; i < 8; ++i)
+                cf[i] = v4f{sa4[i].x * sbv, sa4[i].y * sbv, sa4[i].z * sbv, sa4[i].w * sbv};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const v4f part = mfma<FA, FB>(af[i], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                    acc[i][j][0] = __builtin_fmaf(part[0], c0, acc[i][j][0]);
-                    acc[i][j][1] = __builtin_fmaf(part[1], c1, acc[i][j][1]);
-                    acc[i][j][2] = __builtin_fmaf(part[2], c2, acc[i][j][2]);
-                    acc[i][j][3] = __builtin_fmaf(part[3], c3, acc[i][j][3]);
+            for (int s = 0; s < 64 + kLag; ++s) {
+                if (s < 64) part[s % (kLag + 1)] = mfma<FA, FB>(af[s >> 3], bf[s & 7], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                if (s >= kLag) {
+                    const int q = s - kLag, i = q >> 3, j = q & 7;
+                    const v4f pr = part[q % (kLag + 1)];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i][r], acc[i][j][r]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
