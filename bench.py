@@ -38,6 +38,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TOK, D, F = 65536, 768, 3072   # tokens, d_model, 4 d_model
 LD_PAD = 256                   # bytes of padding per row of the transposed FP8 copies
 FA_M, FA_N, FA_K = 16384, 2048, 7168
+COPY_BYTES = 1 << 30           # calibration copy
 
 
 def parse():
@@ -103,6 +104,21 @@ def main():
     fm.requant_weights([cache], [w_master])
     dw_ws = torch.empty(max(fm.lib().fp8_scaled_mm_workspace_size(F, D, TOK, 0, 0), 1),
                         dtype=torch.uint8, device=dev)
+    # a plain copy of known size (1 GiB read, 1 GiB written) outside the timed
+    # region: the HBM byte counters of the dominant kernel are scaled by what
+    # the same counters read for it, and its rate is this board's copy speed
+    csrc = torch.zeros(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    cdst = torch.empty_like(csrc)
+    torch.neg(csrc, out=cdst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        torch.neg(csrc, out=cdst)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del csrc, cdst
     torch.cuda.synchronize()
 
     # (name, flops, algorithmic HBM bytes, callable)
@@ -180,7 +196,8 @@ def main():
     dflops = [s[1] for s in stages if s[0] == dom][0]
     achieved = dflops / stage_ms[dom] / 1e9
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
 
     counters = ctr.read()
     value = step_flops / (ms_per_step / 1e3) / 1e12
@@ -214,9 +231,49 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "counters": counters,
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out))
+
+
+# Sources each GEMM kernel is compiled from; a stored traffic figure is used
+# only while their hash matches the one it was taken with.
+KERNEL_SOURCES = {
+    "gemm_block_16384x2048x7168": ["gemm.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
+    "gemm_fwd_65536x3072x768": ["gemm_persistent.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
+    "gemm_dx_65536x768x3072": ["gemm_persistent.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
+}
+
+
+def sources_hash(stage: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "fp8_scaled_matmul_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed counter
+    summary profiles/<stage>_traffic.md: FETCH_SIZE + WRITE_SIZE per dispatch
+    (KiB), each scaled by the ratio of the calibration copy's known bytes to
+    what the same counter read for it.  None when no summary exists or the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_traffic.md")
+    if not os.path.exists(path) or stage not in KERNEL_SOURCES:
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+    if rec is None or rec.get("sources_sha256") != sources_hash(stage):
+        return None
+    fetch = rec["fetch_kib"] * 1024.0 * COPY_BYTES / (rec["copy_fetch_kib"] * 1024.0)
+    write = rec["write_kib"] * 1024.0 * COPY_BYTES / (rec["copy_write_kib"] * 1024.0)
+    return round(fetch + write)
 
 
 def cpu_baseline(sample_rows: int, stage_ms: dict):
