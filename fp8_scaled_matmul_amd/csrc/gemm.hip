@@ -1,51 +1,52 @@
 // Scaled FP8 GEMM for gfx950: y = (s_a A_q)(s_b B_q)^T, A [m,k] and B [n,k]
 // both K-contiguous (the TN form _scaled_mm(x, w_fp8, scale_a, scale_b) takes,
 // "#84 FP8 Precision", code excerpt), fp32 accumulation on the CDNA4 FP8
-// matrix cores, bf16 output.  Block-scaled form: per 128-wide K block, the
-// partial product of each 16x16 output tile is promoted into the fp32
-// accumulator with s_a[row, kb] * s_b[n/128, kb] ("fine grained tile and block
-// scaling", "FP8 stability guardrails", section "Real products").
+// matrix cores, bf16 output.  This file holds the block-scaled form (per
+// 128-wide K block, the partial product of each 16x16 output tile is promoted
+// into the fp32 accumulator with s_a[row, kb] * s_b[n/128, kb]: "fine grained
+// tile and block scaling", "FP8 stability guardrails", section "Real
+// products"), the split-K reduction and the launch logic; the per-tensor form
+// is the persistent kernel of gemm_persistent.hip.
 //
-// Design (one workgroup per 256x256 output tile, 4 waves of 128x128):
-//   - K steps of 128 bytes; A and B tiles staged in LDS (2 x 64 KB, double
-//     buffered) with a 16-byte-chunk XOR swizzle that keeps both the row-wise
-//     fills and the fragment reads free of bank conflicts;
-//   - v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales (exponent 127):
-//     every instruction covers exactly one 128-wide K block;
-//   - workgroup ids are spread over the 8 XCDs so that each XCD walks a
-//     contiguous, M-grouped range of output tiles (A panels stay in its L2);
-//   - optional split over K with fp32 partials reduced in a fixed order.
+// Block-scaled design (one workgroup of 8 waves per 256x256 output tile):
+//   - each wave owns 128x64 outputs, so its 128 fp32 accumulators stay in
+//     VGPRs and the promotion is one v_fmac per output and K block, with no
+//     AGPR copies; two waves share each SIMD, so one wave's promotion FMAs
+//     run while the other's MFMAs occupy the matrix core;
+//   - one v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) covers exactly
+//     one K block of a 16x16 tile; its result is promoted three MFMAs later,
+//     when it is written;
+//   - A and B K blocks (2 x 32 KB) are double buffered in LDS, filled by
+//     buffer_load ... lds DMA one K block ahead; s_a arrives by DMA two K
+//     blocks ahead and the workgroup turns it into s_a s_b per row and N block
+//     once, in LDS;
+//   - operand fragments, the next K block's included, are read from LDS
+//     while the MFMAs run; one barrier per K block, after the last read of
+//     the block's own data;
+//   - B rows are permuted in LDS so that each lane ends up with 4 adjacent
+//     output columns (8-byte bf16 stores).
 #include <hip/hip_bf16.h>
 
 #include <algorithm>
 
 #include "device_common.h"
 #include "fp8mi_internal.h"
+#include "gemm_common.h"
 
 namespace fp8mi {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+using gemm::v4f;
+using gemm::v4u;
+using gemm::v8i;
+using gemm::BM;
+using gemm::BN;
+using gemm::BK;
+using gemm::kGroupM;
+using gemm::kTileBytes;
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kGemmThreads = 256;
-constexpr int kGroupM = 8;
-constexpr int kTileBytes = BM * BK;       // 32 KB per operand tile
-
-// 16-byte chunk c (0..7) of row r lives at chunk position swz(r, c).  Any 8
-// consecutive rows reading the same logical chunk land in 8 distinct
-// positions, and any 16 consecutive rows cover all 16 (row parity x
-// position) slots of a 256-byte bank line.
-__device__ inline int swz(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
-
-template <int FA, int FB>
-__device__ inline v4f mfma(const v8i& a, const v8i& b, const v4f& c)
-{
-    // unit block scales: E8M0 exponent 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
-}
+constexpr int kBlockThreads = 512;
 
 struct KArgs {
     const uint8_t* a;
@@ -60,75 +61,9 @@ struct KArgs {
     int splits;
     int ktiles;          // ceil(k / BK)
     int tiles_m, tiles_n;
+    int fast_store;      // 8-byte bf16 (16-byte fp32) stores are aligned
     fp8_counters* ctr;
 };
-
-// Operand tiles move from global memory straight into LDS with
-// buffer_load_dwordx4 ... lds: one instruction fills 1 KB (8 rows of 128
-// bytes) at the wave-uniform LDS address in M0, lane l writing bytes
-// 16 l .. 16 l + 15.  Wave w fills rows 64 w .. 64 w + 63 with 8
-// instructions; the swizzle is applied on the global side by choosing which
-// 16-byte chunk each lane fetches.  Rows past the operand's end fall outside
-// the buffer descriptor's range, and K chunks past k are given an offset
-// outside it: the range check makes both read as zero, with no branches.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-struct TileLoader {
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[8];   // byte offset of this lane's chunk for instruction j, at k0 = 0
-    int ck[2];          // K byte offset of that chunk within a K step (depends on j & 1 only)
-};
-
-__device__ inline TileLoader make_loader(const uint8_t* base, int64_t ld, int row0, int rows)
-{
-    TileLoader L;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t left = (int64_t)rows - row0;
-    const int64_t nrec = left <= 0 ? 0 : std::min<int64_t>(left, BM) * ld;
-    L.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + (int64_t)row0 * ld), (short)0,
-                                               (int)std::min<int64_t>(nrec, 0x7FFFFFF0), 0x00020000);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 64 * w + 8 * j + (l >> 3);
-        const int c = swz(r, l & 7);      // the swizzle is its own inverse
-        L.voff[j] = (uint32_t)(r * ld + 16 * c);
-        if (j < 2) L.ck[j] = 16 * c;
-    }
-    return L;
-}
-
-__device__ inline void issue_tile(const TileLoader& L, uint8_t* lds_tile, int k0, int k)
-{
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t off = k0 + L.ck[j & 1] < k ? L.voff[j] + (uint32_t)k0 : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsrc,
-                                                 (__attribute__((address_space(3))) void*)(lds_tile + (w * 8 + j) * 1024),
-                                                 16, (int)off, 0, 0, 0);
-    }
-}
-
-// MFMA operand fragment for rows row0..row0+15 of a staged tile: lane l holds
-// row row0 + l%16, K bytes 32*(l/16) .. +32 (the same K assignment is used for
-// A and B, so the products pair up element for element).
-__device__ inline v8i load_frag(const uint8_t* lds, int row0)
-{
-    const int l = threadIdx.x & 63;
-    const int r = row0 + (l & 15);
-    const int c0 = (l >> 4) * 2;
-    const uint4 lo = *reinterpret_cast<const uint4*>(lds + r * BK + swz(r, c0) * 16);
-    const uint4 hi = *reinterpret_cast<const uint4*>(lds + r * BK + swz(r, c0 + 1) * 16);
-    v8i f;
-    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-    return f;
-}
-
-__device__ inline uint16_t to_bf16(float v)
-{
-    return __builtin_bit_cast(uint16_t, __float2bfloat16(v));
-}
 
 // Map a linear workgroup id to (split, tile_m, tile_n).  Hardware hands ids
 // to XCDs round robin; re-number so that XCD x owns a contiguous block of
@@ -154,135 +89,266 @@ __device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn)
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_a[2 * kTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) float g_lds_sa[2 * BM];
+__shared__ __attribute__((aligned(16))) float g_lds_sa[4 * BM];       // s_a of 4 K blocks (ring)
+__shared__ __attribute__((aligned(16))) float g_lds_f[4 * 2 * BM];    // s_a s_b: [K block ring][N block][row]
 
-// Per K step and wave: read all 16 operand fragments of the current stage,
-// then start the DMA of the next stage, then run the 64 MFMAs.  Reading
-// before the DMA is issued keeps the compiler from making the reads wait for
-// the DMA (it cannot tell the two stages apart).
-template <int FA, int FB, bool BLOCK>
-__global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(KArgs p)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// buffer_load_dwordx4 ... lds with a wave-uniform byte offset in soffset:
+// lane l's 16 bytes from voff + soff land at lds + 16 l.
+__device__ inline void dma16_so(uint32_t lds, uint32_t voff, const v4u& rsrc, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// DMA geometry of one wave (w = 0..7).  Instruction j (0..3) of an operand
+// fills LDS rows R = 32 w + 8 j + l/8 (1 KB); lane l writes position l%8 of
+// row R, which receives logical chunk swz(R, l%8) of global row g(R).
+// A: g(R) = R.  B: within each 64-row group, g(R) = 4 (R%16) + (R%64)/16, so
+// that lane p of the fragment at LDS rows 16 j' .. 16 j' + 15 of a group
+// carries output column 4 p + j'.  The swizzle depends on R%16, and rows
+// R and R + 16 differ by 16 (A) or 1 (B) global rows: two lane offsets per
+// operand plus a uniform row step cover the 4 instructions.
+struct BlockDma {
+    v4u ra, rb, rs;           // A, B and s_a descriptors of this tile
+    uint32_t va[2], vb[2];    // lane offsets for even and odd j
+    uint32_t vs;              // lane offset of this wave's 64 s_a rows
+    uint32_t step_a, step_b;  // byte step between instructions j and j + 2
+};
+
+__device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0)
+{
+    BlockDma d;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int q = l >> 3, pos = l & 7;
+    const int64_t rows_a = min(p.m - m0, BM), rows_b = min(p.n - n0, BN);
+    d.ra = gemm::make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    d.rb = gemm::make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+    const int nkb = p.k / BK;
+    d.rs = gemm::make_rsrc(p.sa + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb * 4));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int R = 32 * w + 8 * e + q;
+        const int c = gemm::swz(R, pos);
+        d.va[e] = (uint32_t)(R * p.lda + 16 * c);
+        const int g = 64 * (w >> 1) + 32 * e + 4 * q + 2 * (w & 1);
+        d.vb[e] = (uint32_t)(g * p.ldb + 16 * c);
+    }
+    d.vs = (uint32_t)((64 * (w & 3) + l) * nkb * 4);
+    d.step_a = (uint32_t)(16 * p.lda);
+    d.step_b = (uint32_t)p.ldb;
+    return d;
+}
+
+// Instruction j (0..8) of the DMA of K block kb into stage `stage`: 0..3 A,
+// 4..7 B, 8 the s_a column of K block kbs into ring slot kbs & 3 (waves w and
+// w + 4 fetch the same 64 rows).  `live` false turns the instruction into a
+// no-op fill (a zero-length descriptor: every lane reads as zero) so that
+// the K loop needs no branches past the end of the K range.
+__device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb, int kbs, bool live)
+{
+    const int w = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)kb * BK;
+    if (j < 4) {
+        const uint32_t lds = gemm::lds_addr(g_lds_a + stage * kTileBytes + 4096 * w + 1024 * j);
+        v4u r = d.ra;
+        r.z = live ? r.z : 0u;
+        dma16_so(lds, d.va[j & 1], r, __builtin_amdgcn_readfirstlane(k0 + (uint32_t)(j >> 1) * d.step_a));
+    } else if (j < 8) {
+        const int jb = j - 4;
+        const uint32_t lds = gemm::lds_addr(g_lds_b + stage * kTileBytes + 4096 * w + 1024 * jb);
+        v4u r = d.rb;
+        r.z = live ? r.z : 0u;
+        dma16_so(lds, d.vb[jb & 1], r, __builtin_amdgcn_readfirstlane(k0 + (uint32_t)(jb >> 1) * d.step_b));
+    } else {
+        const uint32_t lds = gemm::lds_addr(g_lds_sa + (kbs & 3) * BM + 64 * (w & 3));
+        v4u r = d.rs;
+        r.z = live ? r.z : 0u;
+        gemm::dma4(lds, d.vs + (uint32_t)kbs * 4u, r);
+    }
+}
+
+// s_a s_b of K block kb (ring slot kb & 3) for this tile: thread t handles
+// row t%256 of N block t/256.  s_a of kb is in the s_a ring.  Past the end
+// of the K range (kb >= kb_end) the s_b index is clamped; the slot written
+// is then never read.
+__device__ inline void block_factors(const KArgs& p, int kb, int kb_end, int n0)
+{
+    const int t = threadIdx.x, nbi = t >> 8, row = t & (BM - 1);
+    const int nb = min((n0 >> 7) + nbi, (p.n - 1) >> 7);
+    const int nkb = p.k / BK;
+    const float sbv = p.sb[(int64_t)nb * nkb + min(kb, kb_end - 1)];
+    g_lds_f[(kb & 3) * 2 * BM + nbi * BM + row] = g_lds_sa[(kb & 3) * BM + row] * sbv;
+}
+
+// One K block per iteration.  Slot s (0..31) of a block issues the MFMA of
+// A fragment i = s/4 and B fragment j = s%4, then promotes the result of
+// slot s - 3.  Reads run one fragment group ahead; after the block's last
+// A fragment read (slot 24) every wave waits for its DMA of the next block
+// and meets the others at the barrier of slot 26, after which the next
+// block's DMA target (this block's stage) is free and the next block's data
+// is visible.
+template <int FA, int FB>
+__global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 {
     int split, tm, tn;
     tile_of(p, split, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt_per = (p.ktiles + p.splits - 1) / p.splits;
     const int kt0 = split * kt_per;
-    const int kt1 = min(p.ktiles, kt0 + kt_per);
+    const int ntk = min(p.ktiles, kt0 + kt_per) - kt0;
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * 128;
-    const int wn = (wave & 1) * 128;
-    const int nkb = p.k / BK;   // block-scale columns (k % 128 == 0 in block mode)
-    const int nb = (n0 + wn) / 128;
-    const bool wave_has_cols = n0 + wn < p.n;
+    const int wm = (wave & 1) * 128;
+    const int wn = (wave >> 1) * 64;
+    const int fcol = (wn >> 7) * BM + wm + 4 * (lane >> 4);   // factor row base of this lane
 
-    v4f acc[8][8];
+    v4f acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const TileLoader la_ = make_loader(p.a, p.lda, m0, p.m);
-    const TileLoader lb_ = make_loader(p.b, p.ldb, n0, p.n);
-    if (kt0 < kt1) {
-        issue_tile(la_, g_lds_a, kt0 * BK, p.k);
-        issue_tile(lb_, g_lds_b, kt0 * BK, p.k);
-        if constexpr (BLOCK)
-            g_lds_sa[threadIdx.x] = (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt0] : 0.0f;
-    }
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const uint8_t* la = g_lds_a + buf * kTileBytes;
-        const uint8_t* lb = g_lds_b + buf * kTileBytes;
-        v8i bf[8], af[8];
+    const BlockDma d = block_dma(p, m0, n0);
+    const int kb_end = kt0 + ntk;
+    // prologue: A/B of blocks 0 and 1, s_a of blocks 0, 1, 2
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bf[j] = load_frag(lb, wn + 16 * j);
+    for (int j = 0; j < 8; ++j) block_dma_one(d, j, 0, kt0, 0, true);
+    block_dma_one(d, 8, 0, 0, kt0, true);
+    block_dma_one(d, 8, 0, 0, kt0 + 1, ntk > 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = load_frag(la, wm + 16 * i);
-        float4 sa4[8];
-        float sbv = 0.0f;
-        if constexpr (BLOCK) {
+    for (int j = 0; j < 8; ++j) block_dma_one(d, j, 1, kt0 + 1, 0, ntk > 1);
+    block_dma_one(d, 8, 0, 0, kt0 + 2, ntk > 2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    gemm::barrier_lds();
+    block_factors(p, kt0, kb_end, n0);
+    block_factors(p, kt0 + 1, kb_end, n0);
+    gemm::barrier_lds();
+
+    v8i af[2], bf[4];
+    v4f fc[2], part[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                sa4[i] = *reinterpret_cast<const float4*>(&g_lds_sa[buf * BM + wm + 16 * i + 4 * (lane >> 4)]);
-            sbv = wave_has_cols ? p.sb[(int64_t)nb * nkb + kt] : 0.0f;
-        }
-        if (kt + 1 < kt1) {
-            issue_tile(la_, g_lds_a + (buf ^ 1) * kTileBytes, (kt + 1) * BK, p.k);
-            issue_tile(lb_, g_lds_b + (buf ^ 1) * kTileBytes, (kt + 1) * BK, p.k);
-            if constexpr (BLOCK)
-                g_lds_sa[(buf ^ 1) * BM + threadIdx.x] =
-                    (m0 + (int)threadIdx.x < p.m) ? p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt + 1] : 0.0f;
-        }
-        if constexpr (!BLOCK) {
+    for (int j = 0; j < 4; ++j) bf[j] = gemm::load_frag(g_lds_b, wn + 16 * j);
+    af[0] = gemm::load_frag(g_lds_a, wm);
+    fc[0] = *reinterpret_cast<const v4f*>(&g_lds_f[(kt0 & 3) * 2 * BM + fcol]);
+    fc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < 4; ++e) part[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // No branches inside: past the last block the reads fetch unused data
+    // and the DMA is a no-op fill.
+    for (int t = 0; t < ntk; ++t) {
+        const int kb = kt0 + t;
+        const uint8_t* la = g_lds_a + (t & 1) * kTileBytes;
+        const uint8_t* la_next = g_lds_a + ((t + 1) & 1) * kTileBytes;
+        const uint8_t* lb_next = g_lds_b + ((t + 1) & 1) * kTileBytes;
+        const float* lf = g_lds_f + (kb & 3) * 2 * BM + fcol;
+        const float* lf_next = g_lds_f + ((kb + 1) & 3) * 2 * BM + fcol;
+        const bool live2 = t + 2 < ntk, live3 = t + 3 < ntk;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mfma<FA, FB>(af[i], bf[j], acc[i][j]);
-        } else {
-            // Each MFMA covers one 128-deep K block of a 16x16 tile; its 4
-            // results are promoted kLag MFMAs later, so the FMAs find them
-            // written without the wait states an immediate read would need.
-            constexpr int kLag = 3;
-            v4f part[kLag + 1];
-            v4f cf[8];
+        for (int s = 0; s < 32; ++s) {
+            const int i = s >> 2, j = s & 3;
+            if (j == 0) af[(i + 1) & 1] = gemm::load_frag(i < 7 ? la : la_next, i < 7 ? wm + 16 * (i + 1) : wm);
+            part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            {
+                // promote slot s - 3 (slots 29..31 of the previous block at s < 3)
+                const int q = (s + 29) & 31, iq = q >> 2, jq = q & 3;
+                const v4f pr = part[(s + 1) & 3];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                cf[i] = v4f{sa4[i].x * sbv, sa4[i].y * sbv, sa4[i].z * sbv, sa4[i].w * sbv};
-#pragma unroll
-            for (int s = 0; s < 64 + kLag; ++s) {
-                if (s < 64) part[s % (kLag + 1)] = mfma<FA, FB>(af[s >> 3], bf[s & 7], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                if (s >= kLag) {
-                    const int q = s - kLag, i = q >> 3, j = q & 7;
-                    const v4f pr = part[q % (kLag + 1)];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i][r], acc[i][j][r]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int r = 0; r < 4; ++r) acc[iq][jq][r] = __builtin_fmaf(pr[r], fc[iq & 1][r], acc[iq][jq][r]);
             }
+            // factors of group i + 1: group i - 1's last promotion (slot 4 i - 1) ran at slot 4 i + 2
+            if (j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
+            if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
+            if (s == 26) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                gemm::barrier_lds();
+            }
+            if (s >= 26 && s <= 29) {
+                // A/B of block kb + 2 into this block's stage, two instructions a slot
+                block_dma_one(d, 2 * (s - 26), t & 1, kb + 2, 0, live2);
+                block_dma_one(d, 2 * (s - 26) + 1, t & 1, kb + 2, 0, live2);
+            }
+            if (s == 30) block_dma_one(d, 8, 0, 0, kb + 3, live3);   // s_a of block kb + 3
+            if (s == 27) block_factors(p, kb + 2, kb_end, n0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // promotions of the last block's slots 29..31
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int q = 29 + s, jq = q & 3;
+        const v4f pr = part[(s + 1) & 3];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[7][jq][r] = __builtin_fmaf(pr[r], fc[1][r], acc[7][jq][r]);
+    }
 
-    // epilogue: lane holds column n0+wn+16j+lane%16, rows m0+wm+16i+4(lane/16)+r
-    const int col_l = lane & 15;
-    const int row_l = 4 * (lane >> 4);
+    // epilogue: lane holds columns n0 + wn + 4 (lane%16) + j (j = 0..3) of rows
+    // m0 + wm + 16 i + 4 (lane/16) + r
+    const int col = n0 + wn + 4 * (lane & 15);
+    const int row_l = m0 + wm + 4 * (lane >> 4);
     if (p.ws) {
         float* ws = p.ws + (int64_t)split * p.m * p.n;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int col = n0 + wn + 16 * j + col_l;
-                if (col >= p.n) continue;
+            for (int r = 0; r < 4; ++r) {
+                const int row = row_l + 16 * i + r;
+                if (row >= p.m) continue;
+                if (p.fast_store && col < p.n) {
+                    *reinterpret_cast<float4*>(&ws[(int64_t)row * p.n + col]) =
+                        float4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm + 16 * i + row_l + r;
-                    if (row < p.m) ws[(int64_t)row * p.n + col] = acc[i][j][r];
+                    for (int j = 0; j < 4; ++j)
+                        if (col + j < p.n) ws[(int64_t)row * p.n + col + j] = acc[i][j][r];
                 }
             }
         return;
     }
-    const float scale = BLOCK ? 1.0f : p.sa[0] * p.sb[0];
     uint32_t nonfinite = 0;
+    if (p.fast_store) {
+        const int64_t rows_c = min(p.m - m0, BM);
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc(p.c + (int64_t)m0 * p.ldc, (short)0,
+                                              (int)std::min<int64_t>(rows_c * p.ldc * 2, 0x7FFFFFF0), 0x00020000);
+        const bool col_ok = col < p.n;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = n0 + wn + 16 * j + col_l;
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm + 16 * i + row_l + r;
-                if (row < p.m && col < p.n) {
-                    const uint16_t h = to_bf16(acc[i][j][r] * scale);
-                    nonfinite += (h & 0x7F80u) == 0x7F80u;
-                    p.c[(int64_t)row * p.ldc + col] = h;
-                }
+                const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
+                const uint32_t lo = gemm::pack_bf16(acc[i][0][r], acc[i][1][r]);
+                const uint32_t hi = gemm::pack_bf16(acc[i][2][r], acc[i][3][r]);
+                const bool in = col_ok && m0 + lrow < p.m;
+                // bf16 exponent all ones in any of the 4 halves
+                nonfinite += in ? (((lo & 0x7F80u) == 0x7F80u) + ((lo & 0x7F800000u) == 0x7F800000u) +
+                                   ((hi & 0x7F80u) == 0x7F80u) + ((hi & 0x7F800000u) == 0x7F800000u))
+                                : 0u;
+                const uint32_t off = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : gemm::kOutOfRange;
+                typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 0);
             }
-        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = row_l + 16 * i + r;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (row < p.m && col + j < p.n) {
+                        const uint16_t h = gemm::to_bf16(acc[i][j][r]);
+                        nonfinite += (h & 0x7F80u) == 0x7F80u;
+                        p.c[(int64_t)row * p.ldc + col + j] = h;
+                    }
+            }
+    }
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
 }
 
@@ -297,7 +363,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* ws, int spli
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
         float s = 0.0f;
         for (int sp = 0; sp < splits; ++sp) s += ws[(int64_t)sp * total + i];
-        const uint16_t h = to_bf16(s * scale);
+        const uint16_t h = gemm::to_bf16(s * scale);
         nonfinite += (h & 0x7F80u) == 0x7F80u;
         const int64_t row = i / n, col = i - row * n;
         c[row * ldc + col] = h;
@@ -315,12 +381,9 @@ __global__ void k_zero_bf16(uint16_t* c, int m, int n, int64_t ldc)
 }
 
 template <int FA, int FB>
-hipError_t gemm_fmt(const KArgs& p, bool block, int grid, hipStream_t stream)
+hipError_t gemm_fmt(const KArgs& p, int grid, hipStream_t stream)
 {
-    if (block)
-        hipLaunchKernelGGL((k_gemm<FA, FB, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((k_gemm<FA, FB, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_block<FA, FB>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -397,12 +460,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         return hipGetLastError();
     }
     const int grid = p.tiles_m * p.tiles_n * p.splits;
-    if (g.fa == FP8_E4M3)
-        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, g.block_scaled, grid, stream)
-                             : gemm_fmt<0, 1>(p, g.block_scaled, grid, stream);
+    if (p.ws)
+        p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
     else
-        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, g.block_scaled, grid, stream)
-                             : gemm_fmt<1, 1>(p, g.block_scaled, grid, stream);
+        p.fast_store = (g.n % 4 == 0) && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
+    if (g.fa == FP8_E4M3)
+        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, grid, stream) : gemm_fmt<0, 1>(p, grid, stream);
+    else
+        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, grid, stream) : gemm_fmt<1, 1>(p, grid, stream);
     if (e != hipSuccess || !p.ws) return e;
     const int64_t total = g.m * g.n;
     const int rgrid = (int)std::min<int64_t>((total + 255) / 256, 8192);

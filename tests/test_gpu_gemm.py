@@ -48,7 +48,8 @@ def test_tensor_scaled_small(fa, fb, m, n, k):
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS[:2])
-@pytest.mark.parametrize("m,n,k", [(256, 256, 512), (300, 384, 640), (17, 130, 128), (512, 512, 1024)])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 512), (300, 384, 640), (17, 130, 128), (512, 512, 1024),
+                                   (64, 256, 256), (130, 260, 384)])
 def test_block_scaled_small(fa, fb, m, n, k):
     g = np.random.default_rng(m + n + k)
     av = synth.channel_scaled_bf16(200, 0, 3, (m, k))
