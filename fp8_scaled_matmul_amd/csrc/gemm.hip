@@ -47,6 +47,12 @@ using gemm::kGroupM;
 using gemm::kTileBytes;
 
 constexpr int kBlockThreads = 512;
+// MFMA results are promoted kLag MFMAs after their issue (1..3: at most 4
+// partial tiles live), by which time they are written.
+#ifndef FP8MI_BLOCK_LAG
+#define FP8MI_BLOCK_LAG 3
+#endif
+constexpr int kLag = FP8MI_BLOCK_LAG;
 
 struct KArgs {
     const uint8_t* a;
@@ -91,6 +97,7 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_lds_a[2 * kTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) float g_lds_sa[4 * BM];       // s_a of 4 K blocks (ring)
 __shared__ __attribute__((aligned(16))) float g_lds_f[4 * 2 * BM];    // s_a s_b: [K block ring][N block][row]
+__shared__ __attribute__((aligned(16))) float g_lds_sb[4 * 64];       // s_b of the tile's 2 N blocks (lanes 0, 1)
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -118,12 +125,15 @@ struct BlockDma {
     uint32_t va[2], vb[2];    // lane offsets for even and odd j
     uint32_t vs;              // lane offset of this wave's 64 s_a rows
     uint32_t step_a, step_b;  // byte step between instructions j and j + 2
+    uint32_t lds_a, lds_b, lds_s;   // this wave's LDS targets in stage 0 / ring slot 0 (uniform)
+    v4u rsb;                  // s_b descriptor
+    uint32_t vsb, lds_sb;     // lanes 0, 1: the tile's two N blocks; others out of range
 };
 
-__device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0)
+__device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w)
 {
     BlockDma d;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int l = threadIdx.x & 63;
     const int q = l >> 3, pos = l & 7;
     const int64_t rows_a = min(p.m - m0, BM), rows_b = min(p.n - n0, BN);
     d.ra = gemm::make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
@@ -141,47 +151,51 @@ __device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0)
     d.vs = (uint32_t)((64 * (w & 3) + l) * nkb * 4);
     d.step_a = (uint32_t)(16 * p.lda);
     d.step_b = (uint32_t)p.ldb;
+    d.lds_a = gemm::lds_addr(g_lds_a) + 4096u * w;
+    d.lds_b = gemm::lds_addr(g_lds_b) + 4096u * w;
+    d.lds_s = gemm::lds_addr(g_lds_sa) + 256u * (w & 3);
+    const int nbs = (p.n + 127) / 128;
+    d.rsb = gemm::make_rsrc(p.sb, (uint32_t)(nbs * nkb * 4));
+    d.vsb = l < 2 ? (uint32_t)(((n0 >> 7) + l) * nkb * 4) : gemm::kOutOfRange;
+    d.lds_sb = gemm::lds_addr(g_lds_sb);
     return d;
 }
 
 // Instruction j (0..8) of the DMA of K block kb into stage `stage`: 0..3 A,
-// 4..7 B, 8 the s_a column of K block kbs into ring slot kbs & 3 (waves w and
-// w + 4 fetch the same 64 rows).  `live` false turns the instruction into a
+// 4..7 B, 8 the s_a column and the two s_b values of K block kbs into ring
+// slot kbs & 3 (waves w and w + 4 fetch the same 64 rows; every wave the same
+// s_b pair).  `live` false turns the instruction into a
 // no-op fill (a zero-length descriptor: every lane reads as zero) so that
 // the K loop needs no branches past the end of the K range.
 __device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb, int kbs, bool live)
 {
-    const int w = threadIdx.x >> 6;
     const uint32_t k0 = (uint32_t)kb * BK;
     if (j < 4) {
-        const uint32_t lds = gemm::lds_addr(g_lds_a + stage * kTileBytes + 4096 * w + 1024 * j);
         v4u r = d.ra;
         r.z = live ? r.z : 0u;
-        dma16_so(lds, d.va[j & 1], r, __builtin_amdgcn_readfirstlane(k0 + (uint32_t)(j >> 1) * d.step_a));
+        dma16_so(d.lds_a + stage * kTileBytes + 1024 * j, d.va[j & 1], r, k0 + (uint32_t)(j >> 1) * d.step_a);
     } else if (j < 8) {
         const int jb = j - 4;
-        const uint32_t lds = gemm::lds_addr(g_lds_b + stage * kTileBytes + 4096 * w + 1024 * jb);
         v4u r = d.rb;
         r.z = live ? r.z : 0u;
-        dma16_so(lds, d.vb[jb & 1], r, __builtin_amdgcn_readfirstlane(k0 + (uint32_t)(jb >> 1) * d.step_b));
+        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, d.vb[jb & 1], r, k0 + (uint32_t)(jb >> 1) * d.step_b);
     } else {
-        const uint32_t lds = gemm::lds_addr(g_lds_sa + (kbs & 3) * BM + 64 * (w & 3));
         v4u r = d.rs;
         r.z = live ? r.z : 0u;
-        gemm::dma4(lds, d.vs + (uint32_t)kbs * 4u, r);
+        gemm::dma4(d.lds_s + (kbs & 3) * BM * 4, d.vs + (uint32_t)kbs * 4u, r);
+        v4u rb = d.rsb;
+        rb.z = live ? rb.z : 0u;
+        gemm::dma4(d.lds_sb + (kbs & 3) * 256, d.vsb + (uint32_t)kbs * 4u, rb);
     }
 }
 
-// s_a s_b of K block kb (ring slot kb & 3) for this tile: thread t handles
-// row t%256 of N block t/256.  s_a of kb is in the s_a ring.  Past the end
-// of the K range (kb >= kb_end) the s_b index is clamped; the slot written
-// is then never read.
-__device__ inline void block_factors(const KArgs& p, int kb, int kb_end, int n0)
+// s_a s_b of K block kb (ring slot kb & 3) for this tile: wave w handles
+// rows 64 (w%4) .. +63 of N block w/4.  s_a and s_b of kb are in their LDS
+// rings (zero past the end of the K range, where the slot is never read).
+__device__ inline void block_factors(int kb, int w)
 {
-    const int t = threadIdx.x, nbi = t >> 8, row = t & (BM - 1);
-    const int nb = min((n0 >> 7) + nbi, (p.n - 1) >> 7);
-    const int nkb = p.k / BK;
-    const float sbv = p.sb[(int64_t)nb * nkb + min(kb, kb_end - 1)];
+    const int nbi = w >> 2, row = 64 * (w & 3) + (threadIdx.x & 63);
+    const float sbv = g_lds_sb[(kb & 3) * 64 + nbi];
     g_lds_f[(kb & 3) * 2 * BM + nbi * BM + row] = g_lds_sa[(kb & 3) * BM + row] * sbv;
 }
 
@@ -202,7 +216,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     const int kt0 = split * kt_per;
     const int ntk = min(p.ktiles, kt0 + kt_per) - kt0;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int wm = (wave & 1) * 128;
     const int wn = (wave >> 1) * 64;
@@ -214,8 +228,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const BlockDma d = block_dma(p, m0, n0);
-    const int kb_end = kt0 + ntk;
+    const BlockDma d = block_dma(p, m0, n0, wave);
     // prologue: A/B of blocks 0 and 1, s_a of blocks 0, 1, 2
 #pragma unroll
     for (int j = 0; j < 8; ++j) block_dma_one(d, j, 0, kt0, 0, true);
@@ -226,8 +239,8 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     block_dma_one(d, 8, 0, 0, kt0 + 2, ntk > 2);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     gemm::barrier_lds();
-    block_factors(p, kt0, kb_end, n0);
-    block_factors(p, kt0 + 1, kb_end, n0);
+    block_factors(kt0, wave);
+    block_factors(kt0 + 1, wave);
     gemm::barrier_lds();
 
     v8i af[2], bf[4];
@@ -256,9 +269,9 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             if (j == 0) af[(i + 1) & 1] = gemm::load_frag(i < 7 ? la : la_next, i < 7 ? wm + 16 * (i + 1) : wm);
             part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
             {
-                // promote slot s - 3 (slots 29..31 of the previous block at s < 3)
-                const int q = (s + 29) & 31, iq = q >> 2, jq = q & 3;
-                const v4f pr = part[(s + 1) & 3];
+                // promote slot s - kLag (the previous block's last slots at s < kLag)
+                const int q = (s + 32 - kLag) & 31, iq = q >> 2, jq = q & 3;
+                const v4f pr = part[(s + 4 - kLag) & 3];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[iq][jq][r] = __builtin_fmaf(pr[r], fc[iq & 1][r], acc[iq][jq][r]);
             }
@@ -275,15 +288,15 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                 block_dma_one(d, 2 * (s - 26) + 1, t & 1, kb + 2, 0, live2);
             }
             if (s == 30) block_dma_one(d, 8, 0, 0, kb + 3, live3);   // s_a of block kb + 3
-            if (s == 27) block_factors(p, kb + 2, kb_end, n0);
+            if (s == 27) block_factors(kb + 2, wave);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // promotions of the last block's slots 29..31
+    // promotions of the last block's last kLag slots
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const int q = 29 + s, jq = q & 3;
-        const v4f pr = part[(s + 1) & 3];
+    for (int s = 0; s < kLag; ++s) {
+        const int q = 32 - kLag + s, jq = q & 3;
+        const v4f pr = part[(s + 4 - kLag) & 3];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[7][jq][r] = __builtin_fmaf(pr[r], fc[1][r], acc[7][jq][r]);
     }
