@@ -238,3 +238,29 @@ def requant(master: np.ndarray, fmt: int, gran: int = TENSOR, want_t: bool = Tru
     re-quantized to FP8 and cached for the next forward).  By definition it
     is a fresh quantize of the current master with a current amax scale."""
     return quantize(master, fmt, gran, FROM_AMAX, None, want_t)
+
+
+def quantize_delayed(x: np.ndarray, fmt: int, history, pos: int, want_t: bool = False):
+    """Per-tensor quantize with delayed scaling and an amax history ("FP8
+    stability guardrails", section "Real products": delayed scaling with
+    amax history tracking, the standard FP8 workflow of Transformer Engine).
+
+    Reading taken (the pages name the method only): the history holds the
+    amax values of the last len(history) steps.  The tensor is cast with
+    the scale the current-scaling rule gives for the LARGEST recorded amax
+    (so the tensor's own amax does not enter its own cast), then its amax
+    replaces the entry at `pos`, the oldest one, and `pos` advances
+    cyclically.  Entries are finite and >= 0; an all-zero history gives
+    s = 1, as amax == 0 does.
+
+    Returns (q, q_t or None, scale float32 [1], counters dict,
+    new history float32 array, new pos)."""
+    h = np.asarray(history, dtype=np.float32).reshape(-1)
+    if h.size < 1 or not (0 <= pos < h.size):
+        raise ValueError("history needs >= 1 entry and 0 <= pos < len(history)")
+    s = scale_from_amax(fmt, float(h.max()))
+    q, qt, s_arr, ctr = quantize(x, fmt, TENSOR, GIVEN, np.array([s], dtype=np.float32), want_t)
+    new = h.copy()
+    new[pos] = amax(x, TENSOR)[0]
+    return q, qt, s_arr, ctr, new, (pos + 1) % h.size
+
