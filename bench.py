@@ -149,6 +149,16 @@ def main():
                               out=yf, counters=ctr)),
     ]
     step_flops = sum(s[1] for s in stages)
+    # Measured in the breakdown pass only, not part of the step: the same dY
+    # quantization with delayed scaling (scale from a 16-step amax history,
+    # one read of dY instead of two).
+    dy_hist = fm.AmaxHistory(16, device=dev)
+    dy_ws = torch.empty(fm.lib().fp8_quantize_delayed_workspace_size(TOK, F), dtype=torch.uint8, device=dev)
+    extra = [
+        ("quantize_dy_e5m2_delayed_t", 0, TOK * F * (2 + 1 + 1),
+         lambda: fm.quantize_delayed(dy, fm.E5M2, dy_hist, scale=dys, want_t=True, counters=ctr, out=dyq,
+                                     out_t=dyqt, workspace=dy_ws)),
+    ]
 
     def step(dom_events=None, dom=None):
         # the optimizer's master update precedes the cache refresh (not timed
@@ -172,18 +182,19 @@ def main():
     # events (an event record between two kernels costs the stream a gap of
     # several microseconds, so the timed region below records only around
     # the dominant kernel).
-    stage_ms = {name: 0.0 for name, _, _, _ in stages}
-    for _ in range(args.steps):
-        evs = [new_events() for _ in stages]
-        for i, (name, _, _, fn) in enumerate(stages):
-            evs[i][0].record()
+    stage_ms = {name: 0.0 for name, _, _, _ in stages + extra}
+    evs = [[new_events() for _ in stages + extra] for _ in range(args.steps)]
+    for k in range(args.steps):
+        for i, (name, _, _, fn) in enumerate(stages + extra):
+            evs[k][i][0].record()
             fn()
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        for i, (name, _, _, _) in enumerate(stages):
-            stage_ms[name] += evs[i][0].elapsed_time(evs[i][1]) / args.steps
+            evs[k][i][1].record()
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        for i, (name, _, _, _) in enumerate(stages + extra):
+            stage_ms[name] += evs[k][i][0].elapsed_time(evs[k][i][1]) / args.steps
     kernels = {}
-    for name, flops, nbytes, _ in stages:
+    for name, flops, nbytes, _ in stages + extra:
         ms = stage_ms[name]
         d = {"ms": round(ms, 4)}
         if flops:
@@ -191,6 +202,8 @@ def main():
             d["frac_fp8_peak"] = round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4)
         d["gbs"] = round(nbytes / ms / 1e6, 1)
         d["frac_hbm"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)
+        if name in [e[0] for e in extra]:
+            d["in_step"] = False
         kernels[name] = d
     # dominant kernel: the single-kernel GEMM stage with the largest share
     single_kernel_gemms = ["gemm_fwd_65536x3072x768", "gemm_dx_65536x768x3072", "gemm_block_16384x2048x7168"]

@@ -31,6 +31,7 @@ EXPORTED = [
     "fp8_abi_version", "fp8_status_string", "fp8_last_error",
     "fp8_amax_workspace_size", "fp8_amax",
     "fp8_quantize_workspace_size", "fp8_quantize",
+    "fp8_quantize_delayed_workspace_size", "fp8_quantize_delayed",
     "fp8_scaled_mm_workspace_size", "fp8_scaled_mm",
     "fp8_requant_workspace_size", "fp8_requant_weights",
     "fp8_counters_reset",
@@ -77,6 +78,11 @@ def lib():
         L.fp8_quantize.restype = i32
         L.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, vp,
                                    vp, i64, vp, i64, vp, vp, sz, vp]
+        L.fp8_quantize_delayed_workspace_size.restype = sz
+        L.fp8_quantize_delayed_workspace_size.argtypes = [i64, i64]
+        L.fp8_quantize_delayed.restype = i32
+        L.fp8_quantize_delayed.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp,
+                                           vp, i64, vp, i64, vp, vp, sz, vp]
         L.fp8_scaled_mm_workspace_size.restype = sz
         L.fp8_scaled_mm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
         L.fp8_scaled_mm.restype = i32
@@ -118,6 +124,12 @@ def fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, 
                  workspace, workspace_bytes, stream) -> int:
     return lib().fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
                               workspace, workspace_bytes, stream)
+
+
+def fp8_quantize_delayed(x, dtype, rows, cols, ld, fmt, history, pos, history_len, scale, q, ldq, q_t, ldq_t,
+                         ctr, workspace, workspace_bytes, stream) -> int:
+    return lib().fp8_quantize_delayed(x, dtype, rows, cols, ld, fmt, history, pos, history_len, scale, q, ldq,
+                                      q_t, ldq_t, ctr, workspace, workspace_bytes, stream)
 
 
 def fp8_scaled_mm(a, fa, lda, scale_a, ga, b, fb, ldb, scale_b, gb, m, n, k, c, ldc,
@@ -228,6 +240,43 @@ def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scal
                        scale.data_ptr(), q.data_ptr(), q.stride(0),
                        _ptr(qt), qt.stride(0) if qt is not None else 0,
                        counters.ptr() if counters else None, ws.data_ptr(), wsb, _stream()))
+    return q, qt, scale
+
+
+class AmaxHistory:
+    """Device state of delayed scaling for one tensor: the amax of its last
+    `length` quantizations (float32, zeros at the start) and the slot of the
+    oldest entry (int32)."""
+
+    def __init__(self, length: int = 16, device="cuda"):
+        torch = _torch()
+        self.length = int(length)
+        self.values = torch.zeros(self.length, dtype=torch.float32, device=device)
+        self.pos = torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def quantize_delayed(x, fmt: int, history: AmaxHistory, scale=None, want_t: bool = False,
+                     counters: Counters | None = None, out=None, out_t=None, workspace=None):
+    """Per-tensor quantize with the scale of the recorded amax history, then
+    record this tensor's amax.  Returns (q, q_t or None, scale)."""
+    torch = _torch()
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    q = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    qt = None
+    if want_t:
+        qt = out_t if out_t is not None else torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    wsb = lib().fp8_quantize_delayed_workspace_size(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    check(fp8_quantize_delayed(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), fmt,
+                               history.values.data_ptr(), history.pos.data_ptr(), history.length,
+                               scale.data_ptr(), q.data_ptr(), q.stride(0),
+                               _ptr(qt), qt.stride(0) if qt is not None else 0,
+                               counters.ptr() if counters else None, workspace.data_ptr(), workspace.numel(),
+                               _stream()))
     return q, qt, scale
 
 

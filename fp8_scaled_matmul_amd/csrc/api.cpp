@@ -197,6 +197,44 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
     return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize launch");
 }
 
+size_t fp8_quantize_delayed_workspace_size(int64_t rows, int64_t cols)
+{
+    (void)rows;
+    (void)cols;
+    return kAmaxWorkspaceBytes;
+}
+
+fp8_status fp8_quantize_delayed(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                                fp8_format fmt, float* amax_history, int32_t* history_pos, int32_t history_len,
+                                float* scale, uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                fp8_counters* ctr, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    fp8_status s = check_quantize_args(x, dtype, rows, cols, ld, fmt, FP8_TENSOR, FP8_SCALE_FROM_AMAX, scale, q, ldq,
+                                       q_t, ldq_t, workspace, workspace_bytes);
+    if (s != FP8_OK) return s;
+    if (!amax_history || !history_pos) return fail(FP8_ERR_INVALID_ARG, "amax_history / history_pos: null pointer");
+    if (history_len < 1 || history_len > 4096) return fail(FP8_ERR_INVALID_ARG, "history_len must be in [1, 4096]");
+    if ((s = check_device()) != FP8_OK) return s;
+    QuantArgs a;
+    a.x = x;
+    a.dtype = dtype;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld;
+    a.fmt = fmt;
+    a.gran = FP8_TENSOR;
+    a.mode = FP8_SCALE_GIVEN;
+    a.scale = scale;
+    a.q = q;
+    a.ldq = ldq;
+    a.qt = q_t;
+    a.ldqt = ldq_t;
+    a.ctr = ctr;
+    a.partials = static_cast<uint32_t*>(workspace);
+    hipError_t e = launch_quantize_delayed(a, amax_history, history_pos, history_len, stream);
+    return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize_delayed launch");
+}
+
 size_t fp8_scaled_mm_workspace_size(int64_t m, int64_t n, int64_t k, fp8_granularity ga, fp8_granularity gb)
 {
     (void)ga;

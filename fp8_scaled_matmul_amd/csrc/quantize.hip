@@ -233,6 +233,29 @@ __global__ void __launch_bounds__(kThreads) k_amax_finalize(const uint32_t* part
     if (threadIdx.x == 0) out[0] = key_amax(k);
 }
 
+// Delayed scaling: s from the largest history entry (entries are finite and
+// >= 0, so their bit patterns order like their values).
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) k_delayed_scale(const float* hist, int len, float* scale)
+{
+    const uint32_t k = reduce_partials(reinterpret_cast<const uint32_t*>(hist), len);
+    if (threadIdx.x == 0) scale[0] = scale_from_amax<FMT>(key_amax(k));
+}
+
+// Delayed scaling, after the cast: this tensor's amax (finite maximum, from
+// the partial keys) replaces the oldest history entry; the position advances.
+__global__ void __launch_bounds__(kThreads) k_delayed_record(const uint32_t* partials, int np, float* hist,
+                                                             int32_t* pos, int len)
+{
+    const uint32_t k = reduce_partials(partials, np);
+    if (threadIdx.x == 0) {
+        int p = pos[0] % len;
+        if (p < 0) p += len;
+        hist[p] = key_amax(k);
+        pos[0] = (p + 1) % len;
+    }
+}
+
 // ------------------------------------------------------------------ per-tensor cast
 // Pass 2 of per-tensor scaling (or the whole job with a given scale): every
 // workgroup rebuilds the amax from the partials, derives s, and streams its
@@ -487,7 +510,8 @@ template <int FMT, int SCALE_MODE>
 __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, int64_t rows, int64_t cols,
                                                            int64_t ld, float* scale, const uint32_t* partials,
                                                            int np, uint8_t* q, int64_t ldq, uint8_t* qt,
-                                                           int64_t ldqt, fp8_counters* ctr)
+                                                           int64_t ldqt, fp8_counters* ctr, const float* hist,
+                                                           int hist_len, uint32_t* amax_out)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tt[kTile * kTile];
     const int t = threadIdx.x;
@@ -498,6 +522,20 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
 
     float s_tensor = 1.0f;
     bool special_tensor = true;
+    // SCALE_MODE 3 (delayed scaling): the scale comes from the largest amax
+    // of the history; an element whose |x| pattern exceeds that amax (or is
+    // Inf / NaN) takes the IEEE-division path, the others the corrected
+    // quotient, whose proof covers |x| <= amax for a bf16 amax.
+    uint32_t hist_bits = 0;
+    bool hist_fast = false;
+    us2 seen = us2{0, 0};      // packed |x| pattern max of this thread's elements (mode 3)
+    if constexpr (SCALE_MODE == 3) {
+        const uint32_t hk = reduce_partials(reinterpret_cast<const uint32_t*>(hist), hist_len);
+        s_tensor = scale_from_amax<FMT>(key_amax(hk));
+        if (blockIdx.x == 0 && t == 0) scale[0] = s_tensor;
+        hist_bits = (hk & 0x7FFFFFFFu) >> 16;
+        hist_fast = (hk & 0x8000FFFFu) == 0 && hist_bits < 0x7F80u && s_tensor >= kCorrectedQuotMinScale;
+    }
     if constexpr (SCALE_MODE == 0) {
         if (partials) {
             const uint32_t kk = reduce_partials(partials, np);
@@ -557,6 +595,13 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
             s = scale_from_amax<FMT>(key_amax(key));
             if (t == 0) scale[(r0 / kTile) * tiles_c_all + c0 / kTile] = s;
             fast = !key_special(key) && s >= kCorrectedQuotMinScale;
+        } else if constexpr (SCALE_MODE == 3) {
+            us2 m = us2{0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = pkmax8(m, cur[i]);
+            seen = __builtin_elementwise_max(seen, m);
+            s = s_tensor;
+            fast = hist_fast && (uint32_t)(m.x > m.y ? m.x : m.y) <= hist_bits;   // per thread
         } else {
             s = scale[(r0 / kTile) * tiles_c_all + c0 / kTile];
             fast = false;
@@ -652,6 +697,32 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
         if (id + 1 < id1) load(id + 1, bufa);
         process(bufb, id);
         ++id;
+    }
+    if constexpr (SCALE_MODE == 3) {
+        // this workgroup's amax key for the history; an Inf or NaN among its
+        // elements (rare) makes it read its tiles again for the exact,
+        // flag-carrying merge
+        uint32_t key = pk_raw(seen);
+        if (key >= kRawNonFinite) {
+            key = 0;
+#pragma unroll 1
+            for (int64_t j = id0; j < id1; ++j) {
+                const int64_t r0 = (j / tiles_c) * kTile, c0 = (j % tiles_c) * kTile;
+                const uint16_t* src = x + (r0 + 8 * g) * ld + c0 + 8 * k;
+#pragma unroll 1
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(src + i * ld);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        key = key_merge(key, absbits_bf16(ws[h] & 0xFFFFu));
+                        key = key_merge(key, absbits_bf16(ws[h] >> 16));
+                    }
+                }
+            }
+        }
+        key = block_key_merge(key);
+        if (t == 0) amax_out[blockIdx.x] = key;
     }
     flush_counters_block(ctr, sat, und, nan);
 }
@@ -858,7 +929,7 @@ hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int 
         const int grid = (int)std::min<int64_t>(nfull, (int64_t)num_cus() * 4);
         hipLaunchKernelGGL((k_tile128_bf16<FMT, SCALE_MODE>), dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, parts, np, a.q, a.ldq,
-                           a.qt, a.ldqt, a.ctr);
+                           a.qt, a.ldqt, a.ctr, nullptr, 0, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || nfull == nt) return e;
         only_partial = 1;
@@ -947,6 +1018,61 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)
     if (a.fmt == FP8_E4M3)
         return a.dtype == FP8_IN_BF16 ? quantize_typed<0, 0>(a, stream) : quantize_typed<0, 1>(a, stream);
     return a.dtype == FP8_IN_BF16 ? quantize_typed<1, 0>(a, stream) : quantize_typed<1, 1>(a, stream);
+}
+
+// Delayed scaling.  A bf16 tensor of whole 128x128 tiles with 16-byte rows
+// and a transposed copy takes one pass (cast with the history scale while
+// collecting this tensor's amax); any other layout takes the amax pass, the
+// history scale and a given-scale cast (same bytes, two reads of x).
+hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos, int len, hipStream_t stream)
+{
+    const int64_t rows = a.rows, cols = a.cols;
+    const bool one_pass = a.dtype == FP8_IN_BF16 && a.qt && rows % kTile == 0 && cols % kTile == 0 &&
+                          aligned16(a.x) && aligned16(a.q) && aligned16(a.qt) && (a.ld * 2) % 16 == 0 &&
+                          a.ldq % 8 == 0 && a.ldqt % 16 == 0 && rows > 0 && cols > 0;
+    if (one_pass) {
+        const int64_t nfull = (rows / kTile) * (cols / kTile);
+        const int grid = (int)std::min<int64_t>(nfull, std::min<int64_t>((int64_t)num_cus() * 4, kAmaxPartials));
+        if (a.fmt == FP8_E4M3)
+            hipLaunchKernelGGL((k_tile128_bf16<0, 3>), dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, nullptr, 0, a.q, a.ldq,
+                               a.qt, a.ldqt, a.ctr, hist, len, a.partials);
+        else
+            hipLaunchKernelGGL((k_tile128_bf16<1, 3>), dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, nullptr, 0, a.q, a.ldq,
+                               a.qt, a.ldqt, a.ctr, hist, len, a.partials);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_delayed_record, dim3(1), dim3(kThreads), 0, stream, a.partials, grid, hist, pos, len);
+        return hipGetLastError();
+    }
+    // amax partials of x (its own amax, for the record)
+    const int eb = a.dtype == FP8_IN_BF16 ? 2 : 4;
+    int64_t r = rows, c = cols, l = a.ld;
+    flatten(r, c, l);
+    const int vec = aligned16(a.x) && (r == 1 || (l * eb) % 16 == 0);
+    dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+    if (rows == 0 || cols == 0) { r = 0; g = dim3(1, 1, 1); }
+    if (a.dtype == FP8_IN_BF16)
+        hipLaunchKernelGGL(k_amax_partials<0>, g, dim3(kThreads), 0, stream, a.x, r, c, l, vec, a.partials);
+    else
+        hipLaunchKernelGGL(k_amax_partials<1>, g, dim3(kThreads), 0, stream, a.x, r, c, l, vec, a.partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.fmt == FP8_E4M3)
+        hipLaunchKernelGGL(k_delayed_scale<0>, dim3(1), dim3(kThreads), 0, stream, hist, len, a.scale);
+    else
+        hipLaunchKernelGGL(k_delayed_scale<1>, dim3(1), dim3(kThreads), 0, stream, hist, len, a.scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (rows > 0 && cols > 0) {
+        QuantArgs b = a;
+        b.mode = FP8_SCALE_GIVEN;
+        b.partials = nullptr;
+        if ((e = launch_quantize(b, stream)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_delayed_record, dim3(1), dim3(kThreads), 0, stream, a.partials, (int)(g.x * g.y), hist, pos,
+                       len);
+    return hipGetLastError();
 }
 
 hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* out,

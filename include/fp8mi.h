@@ -135,6 +135,36 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
                         fp8_counters* ctr,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ delayed scaling
+ * Per-tensor quantize with delayed scaling and an amax history (the
+ * guardrails explainer, "Real products": Transformer Engine's delayed
+ * scaling with amax history tracking).  One call:
+ *     s = the FROM_AMAX rule applied to max(amax_history[0 .. history_len))
+ *         (0 -> 1, below FLT_MIN -> FLT_MIN), written to scale[0];
+ *     q (and q_t) = the cast of x with s, exactly as fp8_quantize(GIVEN, s),
+ *         counters included (an element above the recorded amax saturates
+ *         and is counted);
+ *     then amax_history[*history_pos] = amax(x) (finite maximum of |x|) and
+ *         *history_pos = (*history_pos + 1) % history_len.
+ * The tensor's own amax does not enter its own cast; a history of length 1
+ * holding this tensor's amax reproduces fp8_quantize(FROM_AMAX).
+ *   amax_history  device float[history_len], entries finite and >= 0
+ *                 (start from zeros: the first cast then uses s = 1);
+ *   history_pos   device int32, the slot of the oldest entry (taken modulo
+ *                 history_len);  1 <= history_len <= 4096.
+ * A bf16 tensor whose rows and cols are multiples of 128, with 16-byte
+ * aligned rows and a transposed copy, is read once (the cast collects the
+ * amax on the way); other layouts read x twice (amax pass, then cast), with
+ * identical results.  Other arguments as fp8_quantize (TENSOR granularity).
+ * workspace: fp8_quantize_delayed_workspace_size() bytes. */
+size_t     fp8_quantize_delayed_workspace_size(int64_t rows, int64_t cols);
+fp8_status fp8_quantize_delayed(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                                fp8_format fmt, float* amax_history, int32_t* history_pos,
+                                int32_t history_len, float* scale,
+                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                fp8_counters* ctr,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ scaled GEMM
  * y = (s_a A_q)(s_b B_q)^T in the TN layout that _scaled_mm(x, w_fp8,
  * scale_a, scale_b) implies (#84 lab card, code excerpt and "Explanation":

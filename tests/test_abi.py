@@ -130,6 +130,26 @@ def test_amax_and_requant_reject(L):
     assert fm.fp8_counters_reset(None, None) == fm.FP8_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(length=0), fm.FP8_ERR_INVALID_ARG),
+    (dict(length=4097), fm.FP8_ERR_INVALID_ARG),
+    (dict(hist=None), fm.FP8_ERR_INVALID_ARG),
+    (dict(pos=None), fm.FP8_ERR_INVALID_ARG),
+    (dict(ws=None), fm.FP8_ERR_INVALID_ARG),
+    (dict(fmt=4), fm.FP8_ERR_INVALID_ARG),
+    (dict(ld=10), fm.FP8_ERR_INVALID_ARG),
+])
+def test_quantize_delayed_rejects_before_device(L, over, code):
+    a = dict(x=BAD, dtype=0, rows=16, cols=64, ld=64, fmt=0, hist=BAD, pos=BAD, length=16, scale=BAD,
+             q=BAD, ldq=64, q_t=None, ldq_t=0, ctr=None, ws=BAD, wsb=8192)
+    a.update(over)
+    assert L.fp8_quantize_delayed_workspace_size(16, 64) == 8192
+    rc = fm.fp8_quantize_delayed(a["x"], a["dtype"], a["rows"], a["cols"], a["ld"], a["fmt"], a["hist"], a["pos"],
+                                 a["length"], a["scale"], a["q"], a["ldq"], a["q_t"], a["ldq_t"], a["ctr"], a["ws"],
+                                 a["wsb"], None)
+    assert rc == code
+
+
 def test_fastdiv_host(tmp_path):
     """The magic-number division used to map 1x128 tiles to rows."""
     src = tmp_path / "fd.cpp"
