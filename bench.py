@@ -176,6 +176,8 @@ def main():
 
     for _ in range(args.warmup):
         step()
+        for _, _, _, fn in extra:   # also fills the delayed-scaling history
+            fn()
     torch.cuda.synchronize()
 
     # Stage breakdown, outside the timed region: every stage bracketed by
