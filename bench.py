@@ -232,6 +232,7 @@ def main():
 
     counters = ctr.read()
     value = step_flops / (ms_per_step / 1e3) / 1e12
+    bf16 = bf16_matched(torch, x, w_master, dy, stage_ms, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,6 +264,7 @@ def main():
         "kernels": kernels,
         "counters": counters,
         "hbm_copy_gbs": round(copy_gbs, 1),
+        "bf16_matched": bf16,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out))
@@ -305,6 +307,35 @@ def measured_traffic(stage: str):
     fetch = rec["fetch_kib"] * 1024.0 * COPY_BYTES / (rec["copy_fetch_kib"] * 1024.0)
     write = rec["write_kib"] * 1024.0 * COPY_BYTES / (rec["copy_write_kib"] * 1024.0)
     return round(fetch + write)
+
+
+def bf16_matched(torch, x, w, dy, stage_ms: dict, reps: int):
+    """The per-tensor GEMMs of the step in bf16 on the same inputs, through
+    torch's bf16 matmul (hipBLASLt on the MFMA units), timed after the timed
+    region: the FP8 / bf16 speed ratio the pages put at about 2x ("#84 FP8
+    Precision", section "Hardware precision").  Transposed operands are made
+    contiguous beforehand."""
+    wt = w.t().contiguous()          # [768, 3072]
+    dyt = dy.t().contiguous()        # [3072, 65536]
+    cases = [("gemm_fwd_65536x3072x768", lambda: torch.matmul(x, wt)),
+             ("gemm_dx_65536x768x3072", lambda: torch.matmul(dy, w)),
+             ("gemm_dw_3072x768x65536", lambda: torch.matmul(dyt, x))]
+    out = {}
+    for name, fn in cases:
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name] = {"bf16_ms": round(ms, 4), "fp8_ms": round(stage_ms[name], 4),
+                     "fp8_speedup": round(ms / stage_ms[name], 2)}
+    del wt, dyt
+    return out
 
 
 def cpu_baseline(sample_rows: int, stage_ms: dict):
