@@ -12,6 +12,7 @@ definition it follows is cited in ``fp8_oracle.h``.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -263,4 +264,33 @@ def quantize_delayed(x: np.ndarray, fmt: int, history, pos: int, want_t: bool = 
     new = h.copy()
     new[pos] = amax(x, TENSOR)[0]
     return q, qt, s_arr, ctr, new, (pos + 1) % h.size
+
+
+def scale_pow2(fmt: int, amax: float) -> np.float32:
+    """Power-of-two scale of a group: the smallest s = 2^e (e an integer)
+    with amax / s <= fmax, taken on the real quotient; amax == 0 gives 1 and
+    e is raised to -126 (s stays a normal fp32 number, and its exponent field
+    is the E8M0 code the gfx950 scaled MFMA takes).  Not on the pages: the
+    MI355X-native form of their fine-grained tile and block scaling ("FP8
+    stability guardrails", section "Real products"), with the scale
+    restricted to powers of two so that the matrix core can apply it."""
+    a = float(np.float32(amax))
+    if not a > 0.0:
+        return np.float32(1.0)
+    f = fmax(fmt)
+    e = math.frexp(a)[1] - math.frexp(f)[1]
+    while math.ldexp(f, e) < a:          # exact products of a power of two
+        e += 1
+    while math.ldexp(f, e - 1) >= a:
+        e -= 1
+    return np.float32(math.ldexp(1.0, max(e, -126)))
+
+
+def quantize_pow2(x: np.ndarray, fmt: int, gran: int = TENSOR, want_t: bool = False):
+    """Quantize with power-of-two scales: per group, amax (as for FROM_AMAX),
+    s = scale_pow2(amax), then the cast of the GIVEN mode with those scales.
+    Returns (q, q_t or None, scale float32 array, counters dict)."""
+    a = amax(x, gran)
+    s = np.array([scale_pow2(fmt, v) for v in a.reshape(-1)], dtype=np.float32).reshape(a.shape)
+    return quantize(x, fmt, gran, GIVEN, s, want_t)
 
