@@ -25,7 +25,7 @@ FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_UNSUPPORTED_DEVI
 E4M3, E5M2 = 0, 1
 BF16, FP32 = 0, 1
 TENSOR, ROW_1x128, BLOCK_128x128 = 0, 1, 2
-FROM_AMAX, GIVEN = 0, 1
+FROM_AMAX, GIVEN, FROM_AMAX_POW2 = 0, 1, 2
 
 EXPORTED = [
     "fp8_abi_version", "fp8_status_string", "fp8_last_error",

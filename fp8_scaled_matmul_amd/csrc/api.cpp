@@ -64,7 +64,8 @@ fp8_status check_device()
 bool valid_fmt(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 bool valid_dtype(int d) { return d == FP8_IN_BF16 || d == FP8_IN_FP32; }
 bool valid_gran(int g) { return g == FP8_TENSOR || g == FP8_ROW_1x128 || g == FP8_BLOCK_128x128; }
-bool valid_mode(int m) { return m == FP8_SCALE_FROM_AMAX || m == FP8_SCALE_GIVEN; }
+bool valid_mode(int m) { return m == FP8_SCALE_FROM_AMAX || m == FP8_SCALE_GIVEN || m == FP8_SCALE_FROM_AMAX_POW2; }
+bool amax_mode(int m) { return m == FP8_SCALE_FROM_AMAX || m == FP8_SCALE_FROM_AMAX_POW2; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 fp8_status check_2d(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name)
@@ -108,7 +109,7 @@ fp8_status check_quantize_args(const void* x, fp8_dtype dtype, int64_t rows, int
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "tensor too large");
     if (gran == FP8_ROW_1x128 && rows * cdiv(cols, 128) >= ((int64_t)1 << 31))
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many 1x128 tiles");
-    if (gran == FP8_TENSOR && mode == FP8_SCALE_FROM_AMAX &&
+    if (gran == FP8_TENSOR && amax_mode(mode) &&
         (!workspace || workspace_bytes < kAmaxWorkspaceBytes))
         return fail(FP8_ERR_INVALID_ARG, "workspace smaller than fp8_quantize_workspace_size()");
     return FP8_OK;
@@ -165,7 +166,7 @@ size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g
 {
     (void)rows;
     (void)cols;
-    return gran == FP8_TENSOR && mode == FP8_SCALE_FROM_AMAX ? kAmaxWorkspaceBytes : 0;
+    return gran == FP8_TENSOR && amax_mode(mode) ? kAmaxWorkspaceBytes : 0;
 }
 
 fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -185,7 +186,8 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
     a.ld = ld;
     a.fmt = fmt;
     a.gran = gran;
-    a.mode = mode;
+    a.mode = amax_mode(mode) ? FP8_SCALE_FROM_AMAX : mode;
+    a.pow2 = mode == FP8_SCALE_FROM_AMAX_POW2;
     a.scale = scale;
     a.q = q;
     a.ldq = ldq;

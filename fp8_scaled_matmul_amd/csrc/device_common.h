@@ -15,6 +15,7 @@ namespace fp8mi {
 template <int FMT> struct Fmt;
 template <> struct Fmt<0> {
     static constexpr float fmax = 448.0f;
+    static constexpr int fmax_exp = 8;          // 448 = 1.75 * 2^8
     static constexpr uint32_t maxcode = 0x7E;
     // Round-to-nearest-even with no upper exponent bound sends |v| <= 464 to
     // 448 (464 is the tie between 448 and 480, 448 has the even mantissa) and
@@ -26,6 +27,7 @@ template <> struct Fmt<0> {
 };
 template <> struct Fmt<1> {
     static constexpr float fmax = 57344.0f;
+    static constexpr int fmax_exp = 15;         // 57344 = 1.75 * 2^15
     static constexpr uint32_t maxcode = 0x7B;
     // 61440 ties 57344 (odd mantissa) and 65536 (even): rounds up, saturates.
     __device__ static bool saturates(float a) { return a >= 61440.0f; }
@@ -44,6 +46,30 @@ __device__ inline float scale_from_amax(float amax)
     if (amax == 0.0f) return 1.0f;
     float s = amax / Fmt<FMT>::fmax;            // correctly rounded fp32 division
     return s < 0x1p-126f ? 0x1p-126f : s;
+}
+
+// Power-of-two scale: the smallest 2^e with amax / 2^e <= fmax on the real
+// quotient.  With fmax = 1.75 * 2^E and a normal amax = m * 2^ea (m in
+// [1, 2)), that is e = ea - E, plus one when m > 1.75 (fraction bits above
+// 0x600000).  1 for amax 0; e is raised to -126 (amax below FLT_MIN always
+// lands there), so s is a normal number whose exponent field is its E8M0 code.
+template <int FMT>
+__device__ inline float scale_pow2(float amax)
+{
+    if (amax == 0.0f) return 1.0f;
+    if (amax < 0x1p-126f) return 0x1p-126f;
+    const uint32_t b = __builtin_bit_cast(uint32_t, amax);
+    int e = (int)(b >> 23) - 127 - Fmt<FMT>::fmax_exp + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    e = e < -126 ? -126 : e;
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// The scale rule of a FROM_AMAX quantization: fl32(amax / fmax), or the
+// power-of-two rule.
+template <int FMT>
+__device__ inline float scale_rule(float amax, int pow2)
+{
+    return pow2 ? scale_pow2<FMT>(amax) : scale_from_amax<FMT>(amax);
 }
 
 // v = fl32(x / s) for |x| <= amax of the group and s >= 2^-64, from the

@@ -29,6 +29,7 @@ struct QuantArgs {
     int64_t ldqt;
     fp8_counters* ctr;  // nullable
     uint32_t* partials; // per-tensor FROM_AMAX workspace
+    int pow2 = 0;       // FROM_AMAX with the power-of-two scale rule
 };
 
 // Each launcher enqueues on `stream` and returns the hipError_t of the launch.

@@ -304,14 +304,14 @@ template <int FMT, int DT>
 __global__ void __launch_bounds__(kThreads) k_cast_tensor(const void* x, int64_t rows, int64_t cols,
                                                           int64_t ld, int vec, uint8_t* q, int64_t ldq,
                                                           float* scale, const uint32_t* partials, int np,
-                                                          fp8_counters* ctr)
+                                                          fp8_counters* ctr, int pow2)
 {
     float s;
     bool special = true;
     if (partials) {
         const uint32_t k = reduce_partials(partials, np);
         special = key_special(k);
-        s = scale_from_amax<FMT>(key_amax(k));
+        s = scale_rule<FMT>(key_amax(k), pow2);
         if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale[0] = s;
     } else {
         s = scale[0];
@@ -343,7 +343,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
                                                       int64_t ld, int vec, float* scale,
                                                       const uint32_t* partials, int np, uint8_t* q,
                                                       int64_t ldq, uint8_t* qt, int64_t ldqt,
-                                                      fp8_counters* ctr, int only_partial)
+                                                      fp8_counters* ctr, int only_partial, int pow2)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTilePitch];
     const int t = threadIdx.x;
@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
         if (partials) {
             const uint32_t k = reduce_partials(partials, np);
             special_tensor = key_special(k);
-            s_tensor = scale_from_amax<FMT>(key_amax(k));
+            s_tensor = scale_rule<FMT>(key_amax(k), pow2);
             if (blockIdx.x == 0 && t == 0) scale[0] = s_tensor;
         } else {
             s_tensor = scale[0];
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
                 if (t == 0) scale[sidx] = key_amax(key);
                 continue;
             }
-            s = scale_from_amax<FMT>(key_amax(key));
+            s = scale_rule<FMT>(key_amax(key), pow2);
             if (t == 0) scale[sidx] = s;
             fast = DT == 0 && !key_special(key) && s >= kCorrectedQuotMinScale;
         } else {
@@ -511,7 +511,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
                                                            int64_t ld, float* scale, const uint32_t* partials,
                                                            int np, uint8_t* q, int64_t ldq, uint8_t* qt,
                                                            int64_t ldqt, fp8_counters* ctr, const float* hist,
-                                                           int hist_len, uint32_t* amax_out)
+                                                           int hist_len, uint32_t* amax_out, int pow2)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tt[kTile * kTile];
     const int t = threadIdx.x;
@@ -540,7 +540,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
         if (partials) {
             const uint32_t kk = reduce_partials(partials, np);
             special_tensor = key_special(kk);
-            s_tensor = scale_from_amax<FMT>(key_amax(kk));
+            s_tensor = scale_rule<FMT>(key_amax(kk), pow2);
             if (blockIdx.x == 0 && t == 0) scale[0] = s_tensor;
         } else {
             s_tensor = scale[0];
@@ -592,7 +592,7 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
                 }
                 key = block_key_merge_lds(e);
             }
-            s = scale_from_amax<FMT>(key_amax(key));
+            s = scale_rule<FMT>(key_amax(key), pow2);
             if (t == 0) scale[(r0 / kTile) * tiles_c_all + c0 / kTile] = s;
             fast = !key_special(key) && s >= kCorrectedQuotMinScale;
         } else if constexpr (SCALE_MODE == 3) {
@@ -738,7 +738,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, int64_t ld, float* scale,
                                                             uint8_t* q, int64_t ldq, fp8_counters* ctr,
                                                             uint32_t ntiles, FastDiv tiles_per_row,
-                                                            uint32_t scale_ld)
+                                                            uint32_t scale_ld, int pow2)
 {
     constexpr int U = 4;
     constexpr uint32_t kChunk = (kThreads / 16) * U;     // tiles per workgroup and iteration
@@ -784,7 +784,7 @@ __global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, i
         }
         // lane u (u < U) of the group derives the scale of tile u
         const uint32_t mykey = lane == 0 ? key[0] : lane == 1 ? key[1] : lane == 2 ? key[2] : key[3];
-        const float my_s = scale_from_amax<FMT>(key_amax(mykey));
+        const float my_s = scale_rule<FMT>(key_amax(mykey), pow2);
         const float my_r = 1.0f / my_s;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -815,7 +815,7 @@ template <int FMT, int DT, bool GIVEN, bool AMAX_ONLY>
 __global__ void __launch_bounds__(kThreads) k_row1x128(const void* x, int64_t rows, int64_t cols,
                                                        int64_t ld, int vec, float* scale, uint8_t* q,
                                                        int64_t ldq, fp8_counters* ctr, uint32_t ntiles,
-                                                       FastDiv tiles_per_row)
+                                                       FastDiv tiles_per_row, int pow2)
 {
     const int lane = threadIdx.x & 15;
     const uint32_t group = (blockIdx.x * kThreads + threadIdx.x) >> 4;
@@ -848,7 +848,7 @@ __global__ void __launch_bounds__(kThreads) k_row1x128(const void* x, int64_t ro
             s = scale[sidx];
             fast = false;
         } else {
-            s = scale_from_amax<FMT>(key_amax(key));
+            s = scale_rule<FMT>(key_amax(key), pow2);
             if (lane == 0) scale[sidx] = s;
             fast = DT == 0 && !key_special(key) && s >= kCorrectedQuotMinScale;
         }
@@ -929,14 +929,15 @@ hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int 
         const int grid = (int)std::min<int64_t>(nfull, (int64_t)num_cus() * 4);
         hipLaunchKernelGGL((k_tile128_bf16<FMT, SCALE_MODE>), dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, parts, np, a.q, a.ldq,
-                           a.qt, a.ldqt, a.ctr, nullptr, 0, nullptr);
+                           a.qt, a.ldqt, a.ctr, nullptr, 0, nullptr, a.pow2);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || nfull == nt) return e;
         only_partial = 1;
     }
     const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
     hipLaunchKernelGGL((k_tile128<FMT, DT, SCALE_MODE, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
-                       cols, a.ld, vec, a.scale, parts, np, a.q, a.ldq, a.qt, a.ldqt, a.ctr, only_partial);
+                       cols, a.ld, vec, a.scale, parts, np, a.q, a.ldq, a.qt, a.ldqt, a.ctr, only_partial,
+                       a.pow2);
     return hipGetLastError();
 }
 
@@ -971,7 +972,7 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
                             (r == 1 || ((ld * eb) % 16 == 0 && ldq % 16 == 0));
             const dim3 g = stream_grid(r, c, 32, num_cus() * 8);
             hipLaunchKernelGGL((k_cast_tensor<FMT, DT>), g, dim3(kThreads), 0, stream, a.x, r, c, ld, vec,
-                               a.q, ldq, a.scale, parts, np, a.ctr);
+                               a.q, ldq, a.scale, parts, np, a.ctr, a.pow2);
         }
         return hipGetLastError();
     }
@@ -989,16 +990,18 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
         const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16 * 4), (int64_t)num_cus() * 4);
         hipLaunchKernelGGL(k_row1x128_bf16<FMT>, dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.x), a.ld, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles,
-                           FastDiv((uint32_t)tpr), (uint32_t)tpr);
+                           FastDiv((uint32_t)tpr), (uint32_t)tpr, a.pow2);
         return hipGetLastError();
     }
     const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16), (int64_t)num_cus() * 16);
     if (a.mode == FP8_SCALE_FROM_AMAX)
         hipLaunchKernelGGL((k_row1x128<FMT, DT, false, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
-                           cols, a.ld, vec, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles, FastDiv((uint32_t)tpr));
+                           cols, a.ld, vec, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles, FastDiv((uint32_t)tpr),
+                           a.pow2);
     else
         hipLaunchKernelGGL((k_row1x128<FMT, DT, true, false>), dim3(grid), dim3(kThreads), 0, stream, a.x, rows,
-                           cols, a.ld, vec, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles, FastDiv((uint32_t)tpr));
+                           cols, a.ld, vec, a.scale, a.q, a.ldq, a.ctr, (uint32_t)ntiles, FastDiv((uint32_t)tpr),
+                           a.pow2);
     return hipGetLastError();
 }
 
@@ -1036,11 +1039,11 @@ hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos
         if (a.fmt == FP8_E4M3)
             hipLaunchKernelGGL((k_tile128_bf16<0, 3>), dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, nullptr, 0, a.q, a.ldq,
-                               a.qt, a.ldqt, a.ctr, hist, len, a.partials);
+                               a.qt, a.ldqt, a.ctr, hist, len, a.partials, 0);
         else
             hipLaunchKernelGGL((k_tile128_bf16<1, 3>), dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale, nullptr, 0, a.q, a.ldq,
-                               a.qt, a.ldqt, a.ctr, hist, len, a.partials);
+                               a.qt, a.ldqt, a.ctr, hist, len, a.partials, 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_delayed_record, dim3(1), dim3(kThreads), 0, stream, a.partials, grid, hist, pos, len);
@@ -1105,10 +1108,10 @@ hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t c
         const int grid = (int)std::min<int64_t>(nt, (int64_t)num_cus() * 8);
         if (dtype == FP8_IN_BF16)
             hipLaunchKernelGGL((k_tile128<0, 0, 1, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, ld,
-                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
+                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0, 0);
         else
             hipLaunchKernelGGL((k_tile128<0, 1, 1, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, ld,
-                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
+                               vec, out, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0, 0);
         return hipGetLastError();
     }
     const int64_t tpr = cdiv(cols, 128);
@@ -1116,10 +1119,10 @@ hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t c
     const int grid = (int)std::min<int64_t>(cdiv(ntiles, kThreads / 16), (int64_t)num_cus() * 16);
     if (dtype == FP8_IN_BF16)
         hipLaunchKernelGGL((k_row1x128<0, 0, false, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
-                           ld, vec, out, nullptr, 0, nullptr, (uint32_t)ntiles, FastDiv((uint32_t)tpr));
+                           ld, vec, out, nullptr, 0, nullptr, (uint32_t)ntiles, FastDiv((uint32_t)tpr), 0);
     else
         hipLaunchKernelGGL((k_row1x128<0, 1, false, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
-                           ld, vec, out, nullptr, 0, nullptr, (uint32_t)ntiles, FastDiv((uint32_t)tpr));
+                           ld, vec, out, nullptr, 0, nullptr, (uint32_t)ntiles, FastDiv((uint32_t)tpr), 0);
     return hipGetLastError();
 }
 

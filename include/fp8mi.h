@@ -59,7 +59,7 @@ typedef enum {
 typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
 typedef enum { FP8_IN_BF16 = 0, FP8_IN_FP32 = 1 } fp8_dtype;
 typedef enum { FP8_TENSOR = 0, FP8_ROW_1x128 = 1, FP8_BLOCK_128x128 = 2 } fp8_granularity;
-typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
+typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1, FP8_SCALE_FROM_AMAX_POW2 = 2 } fp8_scale_mode;
 
 /* Telemetry ("summary statistics of clipping and overflow events", NanoChat
  * FAQ; "overflow telemetry", guardrails explainer).  Lives in device memory;
@@ -110,6 +110,12 @@ fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, 
  *   mode GIVEN: the caller's scales are READ from `scale` (a "learned" or
  *       fixed scale, #84 lab card, "Hardware precision") and used as they
  *       are; they should be finite and > 0.
+ *   mode FROM_AMAX_POW2: per group, the smallest power of two s with
+ *       amax / s <= fmax (real quotient; 1 for amax 0, at least 2^-126),
+ *       WRITTEN to `scale` as fp32.  Not on the pages: their fine-grained
+ *       scaling with scales the gfx950 MFMA can apply itself (an fp32 power
+ *       of two's exponent field is its E8M0 code); the division is exact and
+ *       nothing saturates.  Such scales feed the _POW2 GEMM pair below.
  *   scale  1 float / [rows, ceil(cols/128)] / [ceil(rows/128), ceil(cols/128)]
  *          row-major, as for fp8_amax.  These are DEQUANTIZATION multipliers
  *          (x ~ s * decode(q)), the scale_a / scale_b of the scaled GEMM.

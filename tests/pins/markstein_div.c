@@ -19,6 +19,10 @@
  * (2^-17), so both values encode to the same signed zero.  The property
  * checked is therefore: v == fl32(x/s) bit for bit, or both have magnitude
  * below 2^-20 and the same sign (same FP8 code and same counter events).
+ * The same check runs over every power-of-two scale the fast path can see
+ * (s = 2^e, -64 <= e <= 121) and every finite bf16 x with |x| <= fmax s,
+ * where it must hold bit for bit with no exception (1/s is exact, so x r is
+ * already the correctly rounded quotient and the correction leaves it).
  * Exit 0 and "OK <n>" on success.
  */
 #include <float.h>
@@ -57,6 +61,31 @@ int main(void)
                     same = 1;                                  /* same signed zero code */
                 if (!same) {
                     if (bad < 5) printf("fmt %d amax %a x %a: %a vs %a\n", fmt, amax, x, v, ref);
+                    bad++;
+                }
+            }
+        }
+    }
+    /* Power-of-two scales (the FROM_AMAX_POW2 rule): every s = 2^e the fast
+     * path can see (2^-64 .. 2^121) and every finite bf16 x with |x| <= fmax s
+     * (a group whose power-of-two scale is s has amax <= fmax s). */
+    for (int fmt = 0; fmt < 2; ++fmt) {
+        #pragma omp parallel for schedule(dynamic, 4) reduction(+:bad, n)
+        for (int e = -64; e <= 121; ++e) {
+            volatile float s = ldexpf(1.0f, e);
+            volatile float r = 1.0f / s;
+            const double lim = (double)fmaxv[fmt] * (double)s;
+            for (uint32_t xb = 0; xb < 0x10000; ++xb) {
+                if ((xb & 0x7F80) == 0x7F80) continue;
+                float x = f_of(xb << 16);
+                if (fabs((double)x) > lim) continue;
+                volatile float q0 = x * r;
+                float ee = fmaf(-q0, s, x);
+                float v = copysignf(fmaf(ee, r, q0), x);
+                volatile float ref = x / s;
+                n++;
+                if (w_of(v) != w_of(ref)) {
+                    if (bad < 5) printf("pow2 fmt %d s 2^%d x %a: %a vs %a\n", fmt, e, x, v, ref);
                     bad++;
                 }
             }
