@@ -154,10 +154,25 @@ def main():
     # one read of dY instead of two).
     dy_hist = fm.AmaxHistory(16, device=dev)
     dy_ws = torch.empty(fm.lib().fp8_quantize_delayed_workspace_size(TOK, F), dtype=torch.uint8, device=dev)
+    # The fine-grained leg with power-of-two scales, which the MFMA applies
+    # itself (E8M0): the same A and B, quantized with the power-of-two rule.
+    aq2 = torch.empty_like(aq)
+    sa2 = torch.empty_like(sa)
+    bq2 = torch.empty_like(bq)
+    sb2 = torch.empty_like(sb)
     extra = [
         ("quantize_dy_e5m2_delayed_t", 0, TOK * F * (2 + 1 + 1),
          lambda: fm.quantize_delayed(dy, fm.E5M2, dy_hist, scale=dys, want_t=True, counters=ctr, out=dyq,
                                      out_t=dyqt, workspace=dy_ws)),
+        ("quantize_a_1x128_pow2", 0, FA_M * FA_K * 3 + FA_M * (FA_K // 128) * 4,
+         lambda: fm.quantize(a_fine, fm.E4M3, fm.ROW_1x128, fm.FROM_AMAX_POW2, scale=sa2, out=aq2, counters=ctr)),
+        ("quantize_b_128x128_pow2", 0, FA_N * FA_K * 3 + (FA_N // 128) * (FA_K // 128) * 4,
+         lambda: fm.quantize(b_fine, fm.E4M3, fm.BLOCK_128x128, fm.FROM_AMAX_POW2, scale=sb2, out=bq2,
+                             counters=ctr)),
+        ("gemm_block_pow2_16384x2048x7168", 2 * FA_M * FA_N * FA_K, FA_M * FA_K + FA_N * FA_K + FA_M * FA_N * 2
+         + FA_M * (FA_K // 128) * 4,
+         lambda: fm.scaled_mm(aq2, fm.E4M3, sa2, fm.ROW_1x128_POW2, bq2, fm.E4M3, sb2, fm.BLOCK_128x128_POW2,
+                              out=yf, counters=ctr)),
     ]
 
     def step(dom_events=None, dom=None):

@@ -25,6 +25,7 @@ FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_UNSUPPORTED_DEVI
 E4M3, E5M2 = 0, 1
 BF16, FP32 = 0, 1
 TENSOR, ROW_1x128, BLOCK_128x128 = 0, 1, 2
+ROW_1x128_POW2, BLOCK_128x128_POW2 = 3, 4      # GEMM operands with power-of-two scales
 FROM_AMAX, GIVEN, FROM_AMAX_POW2 = 0, 1, 2
 
 EXPORTED = [
@@ -183,7 +184,7 @@ def scale_shape(gran: int, rows: int, cols: int) -> tuple[int, ...]:
     nt = -(-cols // 128)
     if gran == TENSOR:
         return (1,)
-    if gran == ROW_1x128:
+    if gran in (ROW_1x128, ROW_1x128_POW2):
         return (rows, nt)
     return (-(-rows // 128), nt)
 

@@ -252,14 +252,16 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda, const flo
                          size_t workspace_bytes, fp8_counters* ctr, hipStream_t stream)
 {
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8_ERR_INVALID_ARG, "unknown FP8 format");
-    if (!valid_gran(ga) || !valid_gran(gb)) return fail(FP8_ERR_INVALID_ARG, "unknown granularity");
+    const bool pow2 = ga == FP8_ROW_1x128_POW2 && gb == FP8_BLOCK_128x128_POW2;
+    if (!pow2 && (!valid_gran(ga) || !valid_gran(gb))) return fail(FP8_ERR_INVALID_ARG, "unknown granularity");
     fp8_status s;
     if ((s = check_2d(a, m, k, lda, "a")) != FP8_OK) return s;
     if ((s = check_2d(b, n, k, ldb, "b")) != FP8_OK) return s;
     if ((s = check_2d(c_bf16, m, n, ldc, "c")) != FP8_OK) return s;
-    const bool block = ga == FP8_ROW_1x128 && gb == FP8_BLOCK_128x128;
+    const bool block = (ga == FP8_ROW_1x128 && gb == FP8_BLOCK_128x128) || pow2;
     if (!block && !(ga == FP8_TENSOR && gb == FP8_TENSOR))
-        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "scale pairs: (TENSOR, TENSOR) or (ROW_1x128, BLOCK_128x128)");
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "scale pairs: (TENSOR, TENSOR), (ROW_1x128, BLOCK_128x128) or "
+                                               "(ROW_1x128_POW2, BLOCK_128x128_POW2)");
     if (block && k % 128 != 0) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "block scaling needs k % 128 == 0");
     // the operand layout rules matter only when operand bytes are read
     const bool reads = m > 0 && n > 0 && k > 0;
@@ -286,6 +288,7 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda, const flo
     g.fa = fa;
     g.fb = fb;
     g.block_scaled = block;
+    g.pow2_scales = pow2;
     g.m = m;
     g.n = n;
     g.k = k;

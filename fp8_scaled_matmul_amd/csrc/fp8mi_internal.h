@@ -49,6 +49,7 @@ struct GemmArgs {
     const float* sb;
     int fa, fb;
     bool block_scaled;
+    bool pow2_scales = false;   // block-scaled with power-of-two scales (E8M0 in the MFMA)
     int64_t m, n, k;
     void* c;
     int64_t ldc;

@@ -98,6 +98,10 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) float g_lds_sa[4 * BM];       // s_a of 4 K blocks (ring)
 __shared__ __attribute__((aligned(16))) float g_lds_f[4 * 2 * BM];    // s_a s_b: [K block ring][N block][row]
 __shared__ __attribute__((aligned(16))) float g_lds_sb[4 * 64];       // s_b of the tile's 2 N blocks (lanes 0, 1)
+// Power-of-two scales: the E8M0 code (fp32 exponent field) of s_a per K block
+// ring slot, laid out [slot][row / 128][row % 16][(row % 128) / 16] so that a
+// lane reads the codes of its 8 A fragments as one 8-byte word.
+__shared__ __attribute__((aligned(16))) uint8_t g_lds_e[4 * 2 * 16 * 8];
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -199,6 +203,29 @@ __device__ inline void block_factors(int kb, int w)
     g_lds_f[(kb & 3) * 2 * BM + nbi * BM + row] = g_lds_sa[(kb & 3) * BM + row] * sbv;
 }
 
+// acc + (2^(ea-127) A)(2^(eb-127) B)^T over one 128-deep K block: byte `sel`
+// of `ea4` is the E8M0 code of this lane's A row, eb the B code.
+template <int FA, int FB>
+__device__ inline v4f mfma_e8m0(int sel, const v8i& a, const v8i& b, const v4f& c, uint32_t ea4, uint32_t eb)
+{
+    switch (sel) {   // the byte select is an immediate of the instruction
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, (int)ea4, 0, (int)eb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 1, (int)ea4, 0, (int)eb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 2, (int)ea4, 0, (int)eb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 3, (int)ea4, 0, (int)eb);
+    }
+}
+
+// Power-of-two scales: the E8M0 codes of s_a of K block kb into their ring
+// slot, one row per lane (waves w and w + 4 write the same row; only the
+// exponent field of each scale is used).
+__device__ inline void block_codes(int kb, int w)
+{
+    const int row = 64 * (w & 3) + (threadIdx.x & 63);
+    const uint32_t code = (__builtin_bit_cast(uint32_t, g_lds_sa[(kb & 3) * BM + row]) >> 23) & 0xFFu;
+    g_lds_e[(kb & 3) * 256 + ((row >> 7) * 16 + (row & 15)) * 8 + ((row & 127) >> 4)] = (uint8_t)code;
+}
+
 // One K block per iteration.  Slot s (0..31) of a block issues the MFMA of
 // A fragment i = s/4 and B fragment j = s%4, then promotes the result of
 // slot s - 3.  Reads run one fragment group ahead; after the block's last
@@ -206,7 +233,10 @@ __device__ inline void block_factors(int kb, int w)
 // and meets the others at the barrier of slot 26, after which the next
 // block's DMA target (this block's stage) is free and the next block's data
 // is visible.
-template <int FA, int FB>
+// E8M0: the scales are powers of two; each MFMA applies them itself (per-lane
+// E8M0 code of its A row, the N block's code for B) and accumulates in
+// place, with no promotion.
+template <int FA, int FB, bool E8M0>
 __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 {
     int split, tm, tn;
@@ -239,8 +269,13 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     block_dma_one(d, 8, 0, 0, kt0 + 2, ntk > 2);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     gemm::barrier_lds();
-    block_factors(kt0, wave);
-    block_factors(kt0 + 1, wave);
+    if constexpr (E8M0) {
+        block_codes(kt0, wave);
+        block_codes(kt0 + 1, wave);
+    } else {
+        block_factors(kt0, wave);
+        block_factors(kt0 + 1, wave);
+    }
     gemm::barrier_lds();
 
     v8i af[2], bf[4];
@@ -252,6 +287,16 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     fc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) part[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // E8M0: this lane's 8 A row codes and the wave's B code, for the current
+    // block (ec, bc) and read ahead for the next (ecn, bcn)
+    const int ecol = (wm >> 7) * 16 + (lane & 15);
+    const int nbi_w = wn >> 7;
+    uint2 ec = uint2{0, 0}, ecn = uint2{0, 0};
+    uint32_t bc = 0, bcn = 0;
+    if constexpr (E8M0) {
+        ec = *reinterpret_cast<const uint2*>(&g_lds_e[(kt0 & 3) * 256 + ecol * 8]);
+        bc = (__builtin_bit_cast(uint32_t, g_lds_sb[(kt0 & 3) * 64 + nbi_w]) >> 23) & 0xFFu;
+    }
 
     // No branches inside: past the last block the reads fetch unused data
     // and the DMA is a no-op fill.
@@ -267,8 +312,16 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
         for (int s = 0; s < 32; ++s) {
             const int i = s >> 2, j = s & 3;
             if (j == 0) af[(i + 1) & 1] = gemm::load_frag(i < 7 ? la : la_next, i < 7 ? wm + 16 * (i + 1) : wm);
-            part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-            {
+            if constexpr (E8M0) {
+                acc[i][j] = mfma_e8m0<FA, FB>(i & 3, af[i & 1], bf[j], acc[i][j], i < 4 ? ec.x : ec.y, bc);
+                if (s == 31) {
+                    ecn = *reinterpret_cast<const uint2*>(&g_lds_e[((kb + 1) & 3) * 256 + ecol * 8]);
+                    bcn = (__builtin_bit_cast(uint32_t, g_lds_sb[((kb + 1) & 3) * 64 + nbi_w]) >> 23) & 0xFFu;
+                }
+            } else {
+                part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            }
+            if constexpr (!E8M0) {
                 // promote slot s - kLag (the previous block's last slots at s < kLag)
                 const int q = (s + 32 - kLag) & 31, iq = q >> 2, jq = q & 3;
                 const v4f pr = part[(s + 4 - kLag) & 3];
@@ -276,7 +329,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                 for (int r = 0; r < 4; ++r) acc[iq][jq][r] = __builtin_fmaf(pr[r], fc[iq & 1][r], acc[iq][jq][r]);
             }
             // factors of group i + 1: group i - 1's last promotion (slot 4 i - 1) ran at slot 4 i + 2
-            if (j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
+            if (!E8M0 && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
             if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
             if (s == 26) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -288,13 +341,22 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                 block_dma_one(d, 2 * (s - 26) + 1, t & 1, kb + 2, 0, live2);
             }
             if (s == 30) block_dma_one(d, 8, 0, 0, kb + 3, live3);   // s_a of block kb + 3
-            if (s == 27) block_factors(kb + 2, wave);
+            if (s == 27) {
+                if constexpr (E8M0)
+                    block_codes(kb + 2, wave);
+                else
+                    block_factors(kb + 2, wave);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (E8M0) {
+            ec = ecn;
+            bc = bcn;
         }
     }
     // promotions of the last block's last kLag slots
 #pragma unroll
-    for (int s = 0; s < kLag; ++s) {
+    for (int s = 0; s < (E8M0 ? 0 : kLag); ++s) {
         const int q = 32 - kLag + s, jq = q & 3;
         const v4f pr = part[(s + 4 - kLag) & 3];
 #pragma unroll
@@ -394,9 +456,12 @@ __global__ void k_zero_bf16(uint16_t* c, int m, int n, int64_t ldc)
 }
 
 template <int FA, int FB>
-hipError_t gemm_fmt(const KArgs& p, int grid, hipStream_t stream)
+hipError_t gemm_fmt(const KArgs& p, int grid, bool e8m0, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_gemm_block<FA, FB>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+    if (e8m0)
+        hipLaunchKernelGGL((k_gemm_block<FA, FB, true>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_gemm_block<FA, FB, false>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -477,10 +542,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
     else
         p.fast_store = (g.n % 4 == 0) && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
+    const bool e8m0 = g.pow2_scales;
     if (g.fa == FP8_E4M3)
-        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, grid, stream) : gemm_fmt<0, 1>(p, grid, stream);
+        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, grid, e8m0, stream) : gemm_fmt<0, 1>(p, grid, e8m0, stream);
     else
-        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, grid, stream) : gemm_fmt<1, 1>(p, grid, stream);
+        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, grid, e8m0, stream) : gemm_fmt<1, 1>(p, grid, e8m0, stream);
     if (e != hipSuccess || !p.ws) return e;
     const int64_t total = g.m * g.n;
     const int rgrid = (int)std::min<int64_t>((total + 255) / 256, 8192);

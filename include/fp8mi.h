@@ -58,7 +58,11 @@ typedef enum {
 
 typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
 typedef enum { FP8_IN_BF16 = 0, FP8_IN_FP32 = 1 } fp8_dtype;
-typedef enum { FP8_TENSOR = 0, FP8_ROW_1x128 = 1, FP8_BLOCK_128x128 = 2 } fp8_granularity;
+typedef enum {
+    FP8_TENSOR = 0, FP8_ROW_1x128 = 1, FP8_BLOCK_128x128 = 2,
+    /* GEMM operands only: 1x128 / 128x128 scales that are powers of two */
+    FP8_ROW_1x128_POW2 = 3, FP8_BLOCK_128x128_POW2 = 4
+} fp8_granularity;
 typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1, FP8_SCALE_FROM_AMAX_POW2 = 2 } fp8_scale_mode;
 
 /* Telemetry ("summary statistics of clipping and overflow events", NanoChat
@@ -183,6 +187,12 @@ fp8_status fp8_quantize_delayed(const void* x, fp8_dtype dtype, int64_t rows, in
  *       ("fine grained tile and block scaling", guardrails explainer,
  *       "Real products"); s_a is [m, k/128], s_b is [ceil(n/128), k/128],
  *       row-major; needs k % 128 == 0.
+ *   (ROW_1x128_POW2, BLOCK_128x128_POW2)  the same sum, for scales that are
+ *       powers of two (as fp8_quantize(FROM_AMAX_POW2) writes them): the
+ *       matrix cores apply them as E8M0 exponents inside each MFMA, with no
+ *       per-block promotion on the VALU.  Only the exponent field of each
+ *       scale is read.  Not on the pages (their fine-grained scaling, in the
+ *       form gfx950's scaled MFMA takes).
  * Products are accumulated in fp32 by the MFMA units; the epilogue rounds to
  * bf16 (nearest even).  Any other pair: FP8_ERR_UNSUPPORTED_SHAPE.
  * Shape rules: k % 16 == 0, lda % 16 == 0, ldb % 16 == 0, a and b 16-byte

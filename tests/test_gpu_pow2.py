@@ -66,3 +66,70 @@ def test_block_scaled_workload_full_size():
     b = synth.channel_scaled_bf16(4, 1, 4, synth.BLOCK_SCALED["b"])
     _cmp_pow2(a, fm.E4M3, fm.ROW_1x128)
     _cmp_pow2(b, fm.E4M3, fm.BLOCK_128x128, want_t=True)
+
+
+# ------------------------------------------------------------------ GEMM with E8M0 scales in the MFMA
+from gpu_util import assert_gemm_close, dev_u8  # noqa: E402
+
+
+def _gemm_pow2(a, fa, sa, b, fb, sb, workspace=True):
+    A, B = dev_u8(a), dev_u8(b)
+    SA, SB = dev_f32(np.asarray(sa, np.float32)), dev_f32(np.asarray(sb, np.float32))
+    ws = None if workspace else torch.empty(0, dtype=torch.uint8, device="cuda")
+    ctr = fm.Counters()
+    y = fm.scaled_mm(A, fa, SA, fm.ROW_1x128_POW2, B, fb, SB, fm.BLOCK_128x128_POW2, counters=ctr, workspace=ws)
+    return host(y), ctr.read()
+
+
+@pytest.mark.parametrize("fa,fb", [(fm.E4M3, fm.E4M3), (fm.E5M2, fm.E4M3), (fm.E4M3, fm.E5M2)])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 512), (300, 384, 640), (17, 130, 128), (512, 512, 1024),
+                                   (64, 256, 256), (130, 260, 384)])
+def test_gemm_pow2_small(fa, fb, m, n, k):
+    av = synth.channel_scaled_bf16(300, 0, 3, (m, k))
+    bv = synth.channel_scaled_bf16(300, 1, 4, (n, k))
+    a, _, sa, _ = oracle.quantize_pow2(av, fa, oracle.ROW_1x128)
+    b, _, sb, _ = oracle.quantize_pow2(bv, fb, oracle.BLOCK_128x128)
+    y, c = _gemm_pow2(a, fa, sa, b, fb, sb)
+    assert_gemm_close(y, oracle.gemm(a, fa, sa, 1, b, fb, sb, 2), f"pow2 {m}x{n}x{k}")
+    assert c["nonfinite_out"] == 0
+
+
+def test_gemm_pow2_split_k_and_no_workspace():
+    m, n, k = 512, 256, 8192
+    av = synth.channel_scaled_bf16(301, 0, 3, (m, k))
+    bv = synth.channel_scaled_bf16(301, 1, 4, (n, k))
+    a, _, sa, _ = oracle.quantize_pow2(av, fm.E5M2, oracle.ROW_1x128)
+    b, _, sb, _ = oracle.quantize_pow2(bv, fm.E4M3, oracle.BLOCK_128x128)
+    ref = oracle.gemm(a, 1, sa, 1, b, 0, sb, 2)
+    y1, _ = _gemm_pow2(a, 1, sa, b, 0, sb)
+    y2, _ = _gemm_pow2(a, 1, sa, b, 0, sb)
+    assert np.array_equal(y1, y2), "not deterministic"
+    assert_gemm_close(y1, ref, "pow2 split-K")
+    y3, _ = _gemm_pow2(a, 1, sa, b, 0, sb, workspace=False)
+    assert_gemm_close(y3, ref, "pow2 no workspace")
+
+
+def test_gemm_pow2_extreme_scales():
+    """Scales far from 1 in both directions (E8M0 codes near both ends)."""
+    m, n, k = 256, 256, 512
+    for sigma in (2.0 ** -100, 2.0 ** 90):
+        av = synth.small_shape_bf16(302, (m, k), sigma)
+        bv = synth.small_shape_bf16(303, (n, k), 1.0 / sigma if sigma < 1 else 2.0 ** -100)
+        a, _, sa, _ = oracle.quantize_pow2(av, fm.E4M3, oracle.ROW_1x128)
+        b, _, sb, _ = oracle.quantize_pow2(bv, fm.E4M3, oracle.BLOCK_128x128)
+        y, _ = _gemm_pow2(a, 0, sa, b, 0, sb)
+        assert_gemm_close(y, oracle.gemm(a, 0, sa, 1, b, 0, sb, 2), f"pow2 sigma {sigma}")
+
+
+def test_gemm_pow2_workload_sampled():
+    a = synth.channel_scaled_bf16(4, 0, 3, synth.BLOCK_SCALED["a"])
+    b = synth.channel_scaled_bf16(4, 1, 4, synth.BLOCK_SCALED["b"])
+    aq, _, sa = fm.quantize(dev_bf16(a), fm.E4M3, fm.ROW_1x128, fm.FROM_AMAX_POW2)
+    bq, _, sb = fm.quantize(dev_bf16(b), fm.E4M3, fm.BLOCK_128x128, fm.FROM_AMAX_POW2)
+    y = host(fm.scaled_mm(aq, 0, sa, fm.ROW_1x128_POW2, bq, 0, sb, fm.BLOCK_128x128_POW2))
+    g = np.random.default_rng(44)
+    m, n = y.shape
+    pm = np.concatenate([g.integers(0, m, 3000), np.full(n, 12345), np.arange(m) % m])
+    pn = np.concatenate([g.integers(0, n, 3000), np.arange(n), np.full(m, 1023)])
+    ref = oracle.gemm_points(host(aq), 0, host(sa), 1, host(bq), 0, host(sb), 2, pm, pn)
+    assert_gemm_close(y[pm, pn], ref, "pow2 block-scaled 16384")
