@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                                 : 0u;
                 const uint32_t off = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : gemm::kOutOfRange;
                 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-                __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 2);   // nontemporal
             }
     } else {
 #pragma unroll

@@ -395,7 +395,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
                     v2u w;
                     w.x = pack_bf16(e0 * out_scale, e1 * out_scale);
                     w.y = pack_bf16(e2 * out_scale, e3 * out_scale);
-                    __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, 0);
+                    // nontemporal (aux bit 1, "nt"): the output streams out (measured:
+                    // 4-8% faster on the 65536-row shapes than the default policy)
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, 2);
                     mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.x & 0x7FFF7FFFu));
                     mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.y & 0x7FFF7FFFu));
                     if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);
