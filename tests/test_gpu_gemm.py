@@ -191,3 +191,37 @@ def test_backward_workload_sampled():
     assert np.array_equal(host(wqt), host(wq).T)
     odq, _, ods, oc = oracle.quantize(dy, fm.E5M2)
     assert np.array_equal(h_dyq, odq) and host(dys)[0] == ods[0]
+
+
+@pytest.mark.parametrize("block", [False, True])
+def test_largest_leading_dimensions(block):
+    """lda, ldb just below 2^22 and ldc just below 2^21 (the limits the C ABI
+    accepts): the 32-bit offsets inside a tile reach their largest values."""
+    m, n, k = 256, 384, 256
+    lda = ldb = (1 << 22) - 16
+    ldc = (1 << 21) - 8
+    g = np.random.default_rng(71)
+    if block:
+        av = synth.channel_scaled_bf16(310, 0, 3, (m, k))
+        bv = synth.channel_scaled_bf16(310, 1, 4, (n, k))
+        a, _, sa, _ = oracle.quantize(av, 0, oracle.ROW_1x128)
+        b, _, sb, _ = oracle.quantize(bv, 0, oracle.BLOCK_128x128)
+        ga, gb = fm.ROW_1x128, fm.BLOCK_128x128
+        ref = oracle.gemm(a, 0, sa, 1, b, 0, sb, 2)
+    else:
+        a, sa = _codes(fm.E4M3, g, (m, k))
+        b, sb = _codes(fm.E4M3, g, (n, k), 0.02)
+        ga = gb = fm.TENSOR
+        ref = oracle.gemm(a, 0, sa, 0, b, 0, sb, 0)
+    A = torch.zeros((m, lda), dtype=torch.uint8, device="cuda")
+    B = torch.zeros((n, ldb), dtype=torch.uint8, device="cuda")
+    A[:, :k].copy_(torch.from_numpy(a))
+    B[:, :k].copy_(torch.from_numpy(b))
+    C = torch.full((m, ldc), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = fm.scaled_mm(A[:, :k], 0, dev_f32(np.asarray(sa, np.float32)), ga, B[:, :k], 0,
+                     dev_f32(np.asarray(sb, np.float32)), gb, out=C[:, :n])
+    assert_gemm_close(host(y), ref, f"ld limits block={block}")
+    # nothing beyond the n output columns of each row was written
+    assert bool((C[:, n:n + 64] == 7.0).all())
+    del A, B, C
+    torch.cuda.empty_cache()
