@@ -22,13 +22,16 @@ constexpr int kTileBytes = BM * BK;     // 32 KB: one operand tile of one K step
 constexpr int kGroupM = 8;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// 16-byte chunk c (0..7) of LDS row r lives at chunk position swz(r, c).
-// Any 8 consecutive rows reading the same logical chunk land in 8 distinct
-// positions, and any 16 consecutive rows cover all 16 (row parity x
-// position) slots of a 256-byte bank line, so fragment reads and the row
-// fills are conflict-free for 32 and for 64 banks.  swz(r, .) is an
-// involution.
-__device__ inline int swz(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
+// 16-byte chunk c (0..7) of the 128-byte LDS row r lives at chunk position
+// swz(r, c) = c ^ f(r), f(r) = (r2, r1, r3) as bits 0..2.  A fragment read
+// (lanes 0..15 rows 16 i + 0..15 at chunk c, lanes 16..31 at chunk c + 2, and
+// so on) then places the 16 lanes of each quarter wave in 16 distinct
+// 16-byte slots of a 256-byte line, and the 32 lanes of each half wave in 32
+// distinct slots of a 512-byte line.  Measured on gfx950 with ds_read_b128:
+// full LDS rate (about 256 bytes per clock per CU), where the earlier
+// f(r) = (r1, r2, r3 ^ r0) pattern, distinct only within quarter waves, ran at
+// half rate.  The row fills write 1 KB contiguous runs.  An involution.
+__device__ inline int swz(int r, int c) { return c ^ (((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4)); }
 
 template <int FA, int FB>
 __device__ inline v4f mfma(const v8i& a, const v8i& b, const v4f& c)
