@@ -127,17 +127,19 @@ __device__ inline uint32_t encode4_general(const float v[4], const float x[4], f
     w = cvt_pk<FMT, true>(clamp_fmax<FMT>(v[2]), clamp_fmax<FMT>(v[3]), w);
     uint32_t out = (uint32_t)w;
     const uint32_t ssign = __builtin_bit_cast(uint32_t, s) >> 31;
+    // Branch-free: with a branch per element the compiler merges the three
+    // counter updates through a pointer select, which moves the counters
+    // into scratch memory (and every update then waits on vector memory).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float a = __builtin_fabsf(v[i]);
-        if (v[i] != v[i]) {
-            const uint32_t sg = (__builtin_bit_cast(uint32_t, x[i]) >> 31) ^ ssign;
-            out = (out & ~(0xFFu << (8 * i))) | (((sg << 7) | 0x7Fu) << (8 * i));
-            nan += 1;
-        } else {
-            sat += Fmt<FMT>::saturates(a);
-            und += (a <= Fmt<FMT>::zero_below_eq) & (x[i] != 0.0f);
-        }
+        const uint32_t isnan = v[i] != v[i];
+        const uint32_t sg = (__builtin_bit_cast(uint32_t, x[i]) >> 31) ^ ssign;
+        const uint32_t nan_code = (out & ~(0xFFu << (8 * i))) | (((sg << 7) | 0x7Fu) << (8 * i));
+        out = isnan ? nan_code : out;
+        nan += isnan;
+        sat += (isnan ^ 1u) & (uint32_t)Fmt<FMT>::saturates(a);
+        und += (isnan ^ 1u) & (uint32_t)(a <= Fmt<FMT>::zero_below_eq) & (uint32_t)(x[i] != 0.0f);
     }
     return out;
 }
