@@ -745,13 +745,13 @@ __global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, i
     const int lane = threadIdx.x & 15;
     const uint32_t gi = threadIdx.x >> 4;                // group in the workgroup
     uint32_t sat = 0, und = 0, nan = 0;
-    // a contiguous range of tiles per workgroup, walked in chunks of 64
-    // consecutive tiles (group gi takes tiles 4 gi .. 4 gi + 3 of a chunk):
-    // consecutive tiles of a row are consecutive in memory
-    const uint32_t per = ((ntiles + gridDim.x - 1) / gridDim.x + kChunk - 1) / kChunk * kChunk;
-    const uint32_t w0 = blockIdx.x * per;
-    const uint32_t g1 = min(ntiles, w0 + per);
-    for (uint32_t t0 = w0 + gi * U; t0 < g1; t0 += kChunk) {
+    // chunks of 64 consecutive tiles (group gi takes tiles 4 gi .. 4 gi + 3 of
+    // a chunk; consecutive tiles of a row are consecutive in memory), dealt
+    // to the workgroups in turn, so the chip streams through one region of
+    // the tensor at a time (measured: 7% faster than a contiguous range of
+    // chunks per workgroup)
+    const uint32_t g1 = ntiles;
+    for (uint32_t t0 = blockIdx.x * kChunk + gi * U; t0 < g1; t0 += kChunk * gridDim.x) {
         uint4 w[U];
         uint32_t row[U], tc[U];
 #pragma unroll
