@@ -104,6 +104,10 @@ __device__ inline float clamp_fmax(float v)
     return __builtin_amdgcn_fmed3f(v, -Fmt<FMT>::fmax, Fmt<FMT>::fmax);
 }
 
+// Unpack bf16 pairs to fp32.
+__device__ inline float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
 // Four quotients (finite, |v| bounded by about fmax) to four codes, plus the
 // count of underflows (non-zero x whose code is +-0).
 template <int FMT>
@@ -115,6 +119,43 @@ __device__ inline uint32_t encode4_fast(const float v[4], const float x[4], uint
     for (int i = 0; i < 4; ++i)
         und += (__builtin_fabsf(v[i]) <= Fmt<FMT>::zero_below_eq) & (x[i] != 0.0f);
     return (uint32_t)w;
+}
+
+// Underflows among four codes (byte i holds element i) of the bf16 inputs in
+// xw0 (elements 0, 1) and xw1 (elements 2, 3): non-zero inputs whose code has
+// magnitude 0.  Byte-parallel: adding 0x7F to a 7-bit magnitude sets bit 7
+// exactly when the magnitude is non-zero (no carry leaves the byte); adding
+// 0x7FFF does the same for each bf16 half, whose high bytes v_perm gathers
+// into code byte order.
+__device__ inline uint32_t underflows4_bf16(uint32_t code, uint32_t xw0, uint32_t xw1)
+{
+    const uint32_t cnz = (code & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+    const uint32_t x0 = (xw0 & 0x7FFF7FFFu) + 0x7FFF7FFFu;
+    const uint32_t x1 = (xw1 & 0x7FFF7FFFu) + 0x7FFF7FFFu;
+    const uint32_t xnz = __builtin_amdgcn_perm(x1, x0, 0x07050301u);   // bytes 1, 3 of x0, then of x1
+    return (uint32_t)__builtin_popcount(xnz & ~cnz & 0x80808080u);
+}
+
+// Eight bf16 inputs (four packed words) to eight codes on the fast path
+// (every quotient finite, scale >= 2^-64): corrected quotient, clamp, packed
+// conversion, and the underflow count taken on the packed words.  A code of
+// magnitude 0 is exactly a quotient with |v| <= half the smallest subnormal
+// (round to nearest even), so this counts what encode4_fast counts.
+template <int FMT>
+__device__ inline uint2 cast8_bf16_fast(const uint32_t ws[4], float s, float r, uint32_t& und)
+{
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        v[2 * h] = clamp_fmax<FMT>(quot_corrected(bf16_lo(ws[h]), s, r));
+        v[2 * h + 1] = clamp_fmax<FMT>(quot_corrected(bf16_hi(ws[h]), s, r));
+    }
+    int w0 = cvt_pk<FMT, false>(v[0], v[1], 0);
+    w0 = cvt_pk<FMT, true>(v[2], v[3], w0);
+    int w1 = cvt_pk<FMT, false>(v[4], v[5], 0);
+    w1 = cvt_pk<FMT, true>(v[6], v[7], w1);
+    und += underflows4_bf16((uint32_t)w0, ws[0], ws[1]) + underflows4_bf16((uint32_t)w1, ws[2], ws[3]);
+    return uint2{(uint32_t)w0, (uint32_t)w1};
 }
 
 // General per-element encode for any quotient (NaN, Inf, out of range), with
@@ -238,8 +279,5 @@ __device__ inline uint32_t wave_key_merge(uint32_t v)
     return v;
 }
 
-// Unpack bf16 pairs to fp32.
-__device__ inline float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 }  // namespace fp8mi

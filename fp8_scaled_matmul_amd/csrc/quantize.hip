@@ -617,9 +617,8 @@ __global__ void __launch_bounds__(kThreads) k_tile128_bf16(const uint16_t* x, in
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint4 w = cur[4 * rb + i];
-                    float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-                    code[i] = cast8<FMT, true>(v, s, r, sat, und, nan);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+                    code[i] = cast8_bf16_fast<FMT>(ws, s, r, und);
                     *reinterpret_cast<uint2*>(qrow + (4 * rb + i) * ldq) = code[i];
                     // one row at a time: keeps the quotient temporaries of the
                     // other rows from being live at once
@@ -801,7 +800,7 @@ __global__ void __launch_bounds__(kThreads) k_row1x128_bf16(const uint16_t* x, i
                 v[2 * h + 1] = bf16_hi(ws[h]);
             }
             const bool fast = !key_special(key[u]) && s >= kCorrectedQuotMinScale;
-            const uint2 o = fast ? cast8<FMT, true>(v, s, r, sat, und, nan) : cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+            const uint2 o = fast ? cast8_bf16_fast<FMT>(ws, s, r, und) : cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
             *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + tc[u] * 128 + lane * 8) = o;
         }
     }
