@@ -141,21 +141,34 @@ __device__ inline uint32_t underflows4_bf16(uint32_t code, uint32_t xw0, uint32_
 // conversion, and the underflow count taken on the packed words.  A code of
 // magnitude 0 is exactly a quotient with |v| <= half the smallest subnormal
 // (round to nearest even), so this counts what encode4_fast counts.
+// The quotient is taken without quot_corrected's copysign: for x != 0 the
+// corrected quotient already has the sign of x (q0 = fl(x r) has it, the
+// correction is smaller than one ulp of q0, and a result that rounds to zero
+// keeps its sign), so only x = -0 comes out as +0; OR-ing the input sign bits
+// into the code bytes restores it and changes no other code.
 template <int FMT>
 __device__ inline uint2 cast8_bf16_fast(const uint32_t ws[4], float s, float r, uint32_t& und)
 {
     float v[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        v[2 * h] = clamp_fmax<FMT>(quot_corrected(bf16_lo(ws[h]), s, r));
-        v[2 * h + 1] = clamp_fmax<FMT>(quot_corrected(bf16_hi(ws[h]), s, r));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float x = e ? bf16_hi(ws[h]) : bf16_lo(ws[h]);
+            const float q0 = x * r;
+            v[2 * h + e] = clamp_fmax<FMT>(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0));
+        }
     }
     int w0 = cvt_pk<FMT, false>(v[0], v[1], 0);
     w0 = cvt_pk<FMT, true>(v[2], v[3], w0);
     int w1 = cvt_pk<FMT, false>(v[4], v[5], 0);
     w1 = cvt_pk<FMT, true>(v[6], v[7], w1);
-    und += underflows4_bf16((uint32_t)w0, ws[0], ws[1]) + underflows4_bf16((uint32_t)w1, ws[2], ws[3]);
-    return uint2{(uint32_t)w0, (uint32_t)w1};
+    // input sign bits (bit 15 and 31 of each word) into code byte order
+    const uint32_t sg0 = __builtin_amdgcn_perm(ws[1], ws[0], 0x07050301u) & 0x80808080u;
+    const uint32_t sg1 = __builtin_amdgcn_perm(ws[3], ws[2], 0x07050301u) & 0x80808080u;
+    const uint32_t c0 = (uint32_t)w0 | sg0, c1 = (uint32_t)w1 | sg1;
+    und += underflows4_bf16(c0, ws[0], ws[1]) + underflows4_bf16(c1, ws[2], ws[3]);
+    return uint2{c0, c1};
 }
 
 // General per-element encode for any quotient (NaN, Inf, out of range), with

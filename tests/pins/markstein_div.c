@@ -23,6 +23,10 @@
  * (s = 2^e, -64 <= e <= 121) and every finite bf16 x with |x| <= fmax s,
  * where it must hold bit for bit with no exception (1/s is exact, so x r is
  * already the correctly rounded quotient and the correction leaves it).
+ * The bf16 fast path of the kernels drops the copysign and ORs the input's
+ * sign bit into the code byte instead; both loops also check that without
+ * the copysign the value is bit-identical for every x != 0 and is a zero
+ * for x = +-0, so that form yields the same codes.
  * Exit 0 and "OK <n>" on success.
  */
 #include <float.h>
@@ -52,9 +56,14 @@ int main(void)
                 float x = f_of(xb << 16);
                 volatile float q0 = x * r;
                 float e = fmaf(-q0, s, x);
-                float v = copysignf(fmaf(e, r, q0), x);
+                float vn = fmaf(e, r, q0);
+                float v = copysignf(vn, x);
                 volatile float ref = x / s;
                 n++;
+                if ((xb & 0x7FFF) ? w_of(vn) != w_of(v) : vn != 0.0f) {
+                    if (bad < 5) printf("no-copysign fmt %d amax %a x %a: %a vs %a\n", fmt, amax, x, vn, v);
+                    bad++;
+                }
                 int same = w_of(v) == w_of(ref);
                 if (!same && fabsf(v) < 0x1p-20f && fabsf(ref) < 0x1p-20f &&
                     signbit(v) == signbit(ref))
@@ -81,9 +90,14 @@ int main(void)
                 if (fabs((double)x) > lim) continue;
                 volatile float q0 = x * r;
                 float ee = fmaf(-q0, s, x);
-                float v = copysignf(fmaf(ee, r, q0), x);
+                float vn = fmaf(ee, r, q0);
+                float v = copysignf(vn, x);
                 volatile float ref = x / s;
                 n++;
+                if ((xb & 0x7FFF) ? w_of(vn) != w_of(v) : vn != 0.0f) {
+                    if (bad < 5) printf("no-copysign pow2 fmt %d s 2^%d x %a: %a vs %a\n", fmt, e, x, vn, v);
+                    bad++;
+                }
                 if (w_of(v) != w_of(ref)) {
                     if (bad < 5) printf("pow2 fmt %d s 2^%d x %a: %a vs %a\n", fmt, e, x, v, ref);
                     bad++;
