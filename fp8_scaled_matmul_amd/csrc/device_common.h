@@ -145,7 +145,11 @@ __device__ inline uint32_t underflows4_bf16(uint32_t code, uint32_t xw0, uint32_
 // corrected quotient already has the sign of x (q0 = fl(x r) has it, the
 // correction is smaller than one ulp of q0, and a result that rounds to zero
 // keeps its sign), so only x = -0 comes out as +0; OR-ing the input sign bits
-// into the code bytes restores it and changes no other code.
+// into the code bytes restores it and changes no other code.  No clamp: with
+// |x| <= amax and s = fl32(amax / fmax) (or a power of two >= amax / fmax),
+// |v| <= fmax (1 + 2^-23), below the midpoint between fmax and the next
+// binade step (464 for E4M3, 61440 for E5M2), so the conversion's round to
+// nearest even already gives +-fmax.
 template <int FMT>
 __device__ inline uint2 cast8_bf16_fast(const uint32_t ws[4], float s, float r, uint32_t& und)
 {
@@ -156,7 +160,7 @@ __device__ inline uint2 cast8_bf16_fast(const uint32_t ws[4], float s, float r, 
         for (int e = 0; e < 2; ++e) {
             const float x = e ? bf16_hi(ws[h]) : bf16_lo(ws[h]);
             const float q0 = x * r;
-            v[2 * h + e] = clamp_fmax<FMT>(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0));
+            v[2 * h + e] = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
         }
     }
     int w0 = cvt_pk<FMT, false>(v[0], v[1], 0);
