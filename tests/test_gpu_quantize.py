@@ -179,3 +179,46 @@ def test_quantize_only_workload_full_size(fmt, gran):
     assert c["saturated"] == 0 and c["nan"] == 0
     if gran == fm.TENSOR and fmt == fm.E4M3:
         assert c["underflow"] > 100000      # scale ~11: many N(0,1) values underflow
+
+
+def _amaxes_over_fmax(fmax, n):
+    """bf16 amaxes whose quotient fl32(amax / s), s = fl32(amax / fmax) raised
+    to FLT_MIN, lands above fmax (IEEE fp32 arithmetic on the host)."""
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint32)
+    a = (bits << 16).view(np.float32)
+    s = np.maximum((a / np.float32(fmax)).astype(np.float32), np.float32(np.finfo(np.float32).tiny))
+    v = (a / s).astype(np.float32)
+    sel = bits[(v > np.float32(fmax)) & (s >= np.float32(2.0 ** -64))]
+    assert sel.size > 1000
+    return sel[np.linspace(0, sel.size - 1, n).astype(int)].astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_amax_quotient_just_above_fmax(fmt):
+    """Groups whose amax element divides to one fp32 ulp above fmax: that
+    element still encodes to +-fmax and nothing counts as saturated (the fast
+    cast leaves this to the conversion's rounding, with no clamp).  Block
+    column j (128 x 128) has amax_j, and every 1x128 row tile in it holds
+    +amax_j or -amax_j, so the 1x128, 128x128 and per-tensor paths all see it."""
+    fmax = 448.0 if fmt == fm.E4M3 else 57344.0
+    top = 0x7E if fmt == fm.E4M3 else 0x7B
+    amaxes = _amaxes_over_fmax(fmax, 16)
+    g = np.random.default_rng(17)
+    rows, nb = 128, amaxes.size
+    x = np.zeros((rows, 128 * nb), dtype=np.uint16)
+    where = g.integers(0, 128, size=(rows, nb))
+    for j, ab in enumerate(amaxes):
+        blk = g.integers(1, int(ab), size=(rows, 128)).astype(np.uint16)
+        blk |= (g.integers(0, 2, size=(rows, 128)) << 15).astype(np.uint16)
+        blk[np.arange(rows), where[:, j]] = ab | ((np.arange(rows) & 1) << 15).astype(np.uint16)
+        x[:, 128 * j:128 * (j + 1)] = blk
+    for gran, want_t in ((fm.ROW_1x128, False), (fm.BLOCK_128x128, True), (fm.BLOCK_128x128, False)):
+        c = _cmp(x, fmt, gran, want_t=want_t)
+        assert c["saturated"] == 0
+        q, _, _, _ = gpu_quantize(dev_bf16(x), fmt, gran, want_t=want_t)
+        codes = q[np.repeat(np.arange(rows), nb), (where + 128 * np.arange(nb)).ravel()]
+        assert np.all((codes & 0x7F) == top), "an amax element did not encode to fmax"
+    for j in range(4):
+        blk = np.ascontiguousarray(x[:, 128 * j:128 * (j + 1)])
+        c = _cmp(blk, fmt, fm.TENSOR, want_t=True)
+        assert c["saturated"] == 0
