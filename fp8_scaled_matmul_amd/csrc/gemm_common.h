@@ -36,8 +36,10 @@ __device__ inline int swz(int r, int c) { return c ^ (((r >> 2) & 1) | (r & 2) |
 template <int FA, int FB>
 __device__ inline v4f mfma(const v8i& a, const v8i& b, const v4f& c)
 {
-    // unit block scales: E8M0 exponent 127 = 2^0; FA / FB: 0 = E4M3, 1 = E5M2
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+    // FA / FB: 0 = E4M3, 1 = E5M2.  Zero scale operands select the unscaled
+    // v_mfma_f32_16x16x128_f8f6f4 (8 bytes), not the scaled form, which is
+    // issued as a v_mfma_ld_scale_b32 prefix plus the MFMA.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 // MFMA operand fragment for LDS rows row0..row0+15 of a staged tile: lane l

@@ -8,7 +8,7 @@
 // wave owns 128x128).  The list of each XCD is a contiguous, M-grouped range,
 // so the A panels and the B operand that the XCD's workgroups share stay in
 // its L2.  The K dimension of all the workgroup's tiles forms one stream of
-// 64-deep half steps; each half step is 16 v_mfma_scale_f32_32x32x64_f8f6f4
+// 64-deep half steps; each half step is 16 v_mfma_f32_32x32x64_f8f6f4
 // per wave.
 //
 // Pipeline (one wave per SIMD, so nothing may stall the MFMA issue):
@@ -81,8 +81,9 @@ __device__ inline int swz4(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3
 template <int FA, int FB>
 __device__ inline v16f mfma32(const v8i& a, const v8i& b, const v16f& c)
 {
-    // unit block scales: E8M0 exponent 127 = 2^0; FA / FB: 0 = E4M3, 1 = E5M2
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+    // FA / FB: 0 = E4M3, 1 = E5M2.  Zero scale operands select the unscaled
+    // v_mfma_f32_32x32x64_f8f6f4 (no v_mfma_ld_scale_b32 prefix).
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 // 32x64 operand fragment of one stage: lane l reads row row0 + l%32, K bytes
