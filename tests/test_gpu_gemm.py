@@ -84,6 +84,27 @@ def test_split_k_and_determinism():
     assert_gemm_close(y, oracle.gemm(a, 0, sa, 1, b, 0, sb, 2), "block split-K")
 
 
+@pytest.mark.parametrize("n,ld_out", [(250, 250), (252, 260), (252, 254)])
+def test_split_k_reduction_layouts(n, ld_out):
+    """Split-K outputs through both reductions: four outputs per thread
+    (n % 4 == 0, output rows 8-byte aligned) and one per thread (ragged n, or
+    an output stride that breaks the 8-byte alignment), into a strided output
+    whose padding columns must stay untouched."""
+    g = np.random.default_rng(n + ld_out)
+    m, k = 300, 4096
+    a, sa = _codes(fm.E5M2, g, (m, k), 1e-3)
+    b, sb = _codes(fm.E4M3, g, (n, k))
+    assert fm.lib().fp8_scaled_mm_workspace_size(m, n, k, 0, 0) > 0
+    full = torch.full((m, ld_out), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = full[:, :n]
+    SA, SB = dev_f32(np.asarray(sa, np.float32).reshape(-1)), dev_f32(np.asarray(sb, np.float32).reshape(-1))
+    fm.scaled_mm(dev_u8(a), fm.E5M2, SA, 0, dev_u8(b), fm.E4M3, SB, 0, out=out)
+    y = host(out.contiguous())
+    assert_gemm_close(y, oracle.gemm(a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0), f"split-K n={n} ldc={ld_out}")
+    if ld_out > n:
+        assert torch.all(full[:, n:] == 3.0), "split-K reduction wrote past the output columns"
+
+
 def test_k_zero_and_empty():
     A = torch.zeros((8, 0), dtype=torch.uint8, device="cuda")
     B = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
