@@ -143,6 +143,8 @@ struct Cursor {
     Item it;
     int h;
     bool valid;
+    v4u ra, rb;     // the item's A and B panels (zero length once the stream has ended),
+                    // formed once per item rather than for every half step's DMA job
 };
 
 __device__ inline void cursor_load(const PArgs& p, Cursor& c, int xcd, int slot)
@@ -156,6 +158,8 @@ __device__ inline void cursor_load(const PArgs& p, Cursor& c, int xcd, int slot)
         c.it = Item{0, 0, 0, 0, 0};
         c.h = 0;
     }
+    c.ra = make_rsrc(p.a + (int64_t)c.it.m0 * p.lda, c.valid ? (uint32_t)(min(BM, p.m - c.it.m0) * p.lda) : 0u);
+    c.rb = make_rsrc(p.b + (int64_t)c.it.n0 * p.ldb, c.valid ? (uint32_t)(min(BN, p.n - c.it.n0) * p.ldb) : 0u);
 }
 
 __device__ inline void cursor_next(const PArgs& p, Cursor& c, int xcd, int slot)
@@ -306,9 +310,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_persistent(PArgs p)
     auto make_job = [&](int stage) -> DmaJob {
         DmaJob job;
         const bool v = d.valid;
-        const Item& it = d.it;
-        job.ra = make_rsrc(p.a + (int64_t)it.m0 * p.lda, v ? (uint32_t)(min(BM, p.m - it.m0) * p.lda) : 0u);
-        job.rb = make_rsrc(p.b + (int64_t)it.n0 * p.ldb, v ? (uint32_t)(min(BN, p.n - it.n0) * p.ldb) : 0u);
+        job.ra = d.ra;
+        job.rb = d.rb;
         job.lds_a = lds_a0 + stage * kStageBytes + wave_slot;
         job.lds_b = lds_b0 + stage * kStageBytes + wave_slot;
         job.k0 = d.h * KH;
