@@ -17,12 +17,12 @@
 //     one K block of a 16x16 tile; its result is promoted three MFMAs later,
 //     when it is written;
 //   - A and B K blocks (2 x 32 KB) are double buffered in LDS, filled by
-//     buffer_load ... lds DMA one K block ahead; s_a arrives by DMA two K
-//     blocks ahead and the workgroup turns it into s_a s_b per row and N block
-//     once, in LDS;
+//     buffer_load ... lds DMA: B early in the block two K blocks ahead, A
+//     after the block's last A read; s_a arrives by DMA two K blocks ahead and
+//     the workgroup turns it into s_a s_b per row and N block once, in LDS;
 //   - operand fragments, the next K block's included, are read from LDS
-//     while the MFMAs run; one barrier per K block, after the last read of
-//     the block's own data;
+//     while the MFMAs run; two barriers per K block: one once every wave
+//     holds the block's B fragments, one after the last read of its A data;
 //   - B rows are permuted in LDS so that each lane ends up with 4 adjacent
 //     output columns (8-byte bf16 stores).
 #include <hip/hip_bf16.h>
@@ -228,11 +228,12 @@ __device__ inline void block_codes(int kb, int w)
 
 // One K block per iteration.  Slot s (0..31) of a block issues the MFMA of
 // A fragment i = s/4 and B fragment j = s%4, then promotes the result of
-// slot s - 3.  Reads run one fragment group ahead; after the block's last
+// slot s - 3.  Reads run one fragment group ahead.  At slot 1 the waves meet
+// once every wave holds this block's B fragments: the B half of this
+// block's stage then takes the B DMA of block kb + 2.  After the block's last
 // A fragment read (slot 24) every wave waits for its DMA of the next block
-// and meets the others at the barrier of slot 26, after which the next
-// block's DMA target (this block's stage) is free and the next block's data
-// is visible.
+// and meets the others at the barrier of slot 26, after which the A half is
+// free for block kb + 2 and the next block's data is visible.
 // E8M0: the scales are powers of two; each MFMA applies them itself (per-lane
 // E8M0 code of its A row, the N block's code for B) and accumulates in
 // place, with no promotion.
@@ -331,12 +332,19 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             // factors of group i + 1: group i - 1's last promotion (slot 4 i - 1) ran at slot 4 i + 2
             if (!E8M0 && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
             if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
+            // B of block kb + 2 early in the block: this block's B fragments are
+            // already in registers once every wave has passed the barrier of
+            // slot 1, so the stage's B half is free; A follows at slot 26, after
+            // the block's last A read.  The delivery of the two halves is spread
+            // over the block, and B is requested almost two blocks ahead.
+            if (s == 1) gemm::barrier_lds();
+            if (s >= 2 && s <= 5) block_dma_one(d, 4 + (s - 2), t & 1, kb + 2, 0, live2);
             if (s == 26) {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                // everything but this block's 4 B instructions (loads complete in order)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
                 gemm::barrier_lds();
             }
-            if (s >= 26 && s <= 29) {
-                // A/B of block kb + 2 into this block's stage, two instructions a slot
+            if (s >= 26 && s <= 27) {
                 block_dma_one(d, 2 * (s - 26), t & 1, kb + 2, 0, live2);
                 block_dma_one(d, 2 * (s - 26) + 1, t & 1, kb + 2, 0, live2);
             }
