@@ -5,8 +5,9 @@
 // 128-wide K block, the partial product of each 16x16 output tile is promoted
 // into the fp32 accumulator with s_a[row, kb] * s_b[n/128, kb]: "fine grained
 // tile and block scaling", "FP8 stability guardrails", section "Real
-// products"), the split-K reduction and the launch logic; the per-tensor form
-// is the persistent kernel of gemm_persistent.hip.
+// products"), the same kernel with per-tensor scales for K splits, the
+// split-K reduction and the launch logic; the other per-tensor GEMMs run the
+// persistent kernel of gemm_persistent.hip.
 //
 // Block-scaled design (one workgroup of 8 waves per 256x256 output tile):
 //   - each wave owns 128x64 outputs, so its 128 fp32 accumulators stay in
@@ -47,6 +48,7 @@ using gemm::kGroupM;
 using gemm::kTileBytes;
 
 constexpr int kBlockThreads = 512;
+constexpr int kModeBlock = 0, kModeE8M0 = 1, kModeTensor = 2;   // scales: fp32 blocks, E8M0 blocks, per tensor
 // MFMA results are promoted kLag MFMAs after their issue (1..3: at most 4
 // partial tiles live), by which time they are written.
 #ifndef FP8MI_BLOCK_LAG
@@ -134,7 +136,7 @@ struct BlockDma {
     uint32_t vsb, lds_sb;     // lanes 0, 1: the tile's two N blocks; others out of range
 };
 
-__device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w)
+__device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w, bool block_scales)
 {
     BlockDma d;
     const int l = threadIdx.x & 63;
@@ -143,7 +145,8 @@ __device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w)
     d.ra = gemm::make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
     d.rb = gemm::make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
     const int nkb = p.k / BK;
-    d.rs = gemm::make_rsrc(p.sa + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb * 4));
+    // per-tensor scales: no scale blocks to fetch (zero-length descriptors)
+    d.rs = gemm::make_rsrc(p.sa + (int64_t)m0 * nkb, block_scales ? (uint32_t)(rows_a * nkb * 4) : 0u);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int R = 32 * w + 8 * e + q;
@@ -159,7 +162,7 @@ __device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w)
     d.lds_b = gemm::lds_addr(g_lds_b) + 4096u * w;
     d.lds_s = gemm::lds_addr(g_lds_sa) + 256u * (w & 3);
     const int nbs = (p.n + 127) / 128;
-    d.rsb = gemm::make_rsrc(p.sb, (uint32_t)(nbs * nkb * 4));
+    d.rsb = gemm::make_rsrc(p.sb, block_scales ? (uint32_t)(nbs * nkb * 4) : 0u);
     d.vsb = l < 2 ? (uint32_t)(((n0 >> 7) + l) * nkb * 4) : gemm::kOutOfRange;
     d.lds_sb = gemm::lds_addr(g_lds_sb);
     return d;
@@ -234,12 +237,19 @@ __device__ inline void block_codes(int kb, int w)
 // A fragment read (slot 24) every wave waits for its DMA of the next block
 // and meets the others at the barrier of slot 26, after which the A half is
 // free for block kb + 2 and the next block's data is visible.
-// E8M0: the scales are powers of two; each MFMA applies them itself (per-lane
-// E8M0 code of its A row, the N block's code for B) and accumulates in
-// place, with no promotion.
-template <int FA, int FB, bool E8M0>
+// MODE kModeE8M0: the scales are powers of two; each MFMA applies them
+// itself (per-lane E8M0 code of its A row, the N block's code for B) and
+// accumulates in place, with no promotion.  MODE kModeTensor: one scale per
+// operand; the MFMAs accumulate in place and the epilogue (or the split-K
+// reduction) multiplies by s_a s_b.
+template <int FA, int FB, int MODE>
 __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 {
+    constexpr bool E8M0 = MODE == kModeE8M0;
+    constexpr bool TENSOR = MODE == kModeTensor;
+    constexpr bool PROMOTE = MODE == kModeBlock;
+    // the per-tensor output scale, read before any DMA is in flight
+    const float out_scale = (TENSOR && !p.ws) ? p.sa[0] * p.sb[0] : 1.0f;
     int split, tm, tn;
     tile_of(p, split, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -259,7 +269,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const BlockDma d = block_dma(p, m0, n0, wave);
+    const BlockDma d = block_dma(p, m0, n0, wave, !TENSOR);
     // prologue: A/B of blocks 0 and 1, s_a of blocks 0, 1, 2
 #pragma unroll
     for (int j = 0; j < 8; ++j) block_dma_one(d, j, 0, kt0, 0, true);
@@ -273,7 +283,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     if constexpr (E8M0) {
         block_codes(kt0, wave);
         block_codes(kt0 + 1, wave);
-    } else {
+    } else if constexpr (PROMOTE) {
         block_factors(kt0, wave);
         block_factors(kt0 + 1, wave);
     }
@@ -319,10 +329,12 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                     ecn = *reinterpret_cast<const uint2*>(&g_lds_e[((kb + 1) & 3) * 256 + ecol * 8]);
                     bcn = (__builtin_bit_cast(uint32_t, g_lds_sb[((kb + 1) & 3) * 64 + nbi_w]) >> 23) & 0xFFu;
                 }
+            } else if constexpr (TENSOR) {
+                acc[i][j] = gemm::mfma<FA, FB>(af[i & 1], bf[j], acc[i][j]);
             } else {
                 part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
             }
-            if constexpr (!E8M0) {
+            if constexpr (PROMOTE) {
                 // promote slot s - kLag (the previous block's last slots at s < kLag)
                 const int q = (s + 32 - kLag) & 31, iq = q >> 2, jq = q & 3;
                 const v4f pr = part[(s + 4 - kLag) & 3];
@@ -330,7 +342,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                 for (int r = 0; r < 4; ++r) acc[iq][jq][r] = __builtin_fmaf(pr[r], fc[iq & 1][r], acc[iq][jq][r]);
             }
             // factors of group i + 1: group i - 1's last promotion (slot 4 i - 1) ran at slot 4 i + 2
-            if (!E8M0 && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
+            if (PROMOTE && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
             if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
             // B of block kb + 2 early in the block: this block's B fragments are
             // already in registers once every wave has passed the barrier of
@@ -352,7 +364,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             if (s == 27) {
                 if constexpr (E8M0)
                     block_codes(kb + 2, wave);
-                else
+                else if constexpr (PROMOTE)
                     block_factors(kb + 2, wave);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -364,7 +376,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     }
     // promotions of the last block's last kLag slots
 #pragma unroll
-    for (int s = 0; s < (E8M0 ? 0 : kLag); ++s) {
+    for (int s = 0; s < (PROMOTE ? kLag : 0); ++s) {
         const int q = 32 - kLag + s, jq = q & 3;
         const v4f pr = part[(s + 4 - kLag) & 3];
 #pragma unroll
@@ -406,8 +418,8 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
-                const uint32_t lo = gemm::pack_bf16(acc[i][0][r], acc[i][1][r]);
-                const uint32_t hi = gemm::pack_bf16(acc[i][2][r], acc[i][3][r]);
+                const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * out_scale, acc[i][1][r] * out_scale);
+                const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * out_scale, acc[i][3][r] * out_scale);
                 const bool in = col_ok && m0 + lrow < p.m;
                 // bf16 exponent all ones in any of the 4 halves
                 nonfinite += in ? (((lo & 0x7F80u) == 0x7F80u) + ((lo & 0x7F800000u) == 0x7F800000u) +
@@ -426,7 +438,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (row < p.m && col + j < p.n) {
-                        const uint16_t h = gemm::to_bf16(acc[i][j][r]);
+                        const uint16_t h = gemm::to_bf16(acc[i][j][r] * out_scale);
                         nonfinite += (h & 0x7F80u) == 0x7F80u;
                         p.c[(int64_t)row * p.ldc + col + j] = h;
                     }
@@ -512,12 +524,14 @@ hipError_t launch_reduce(const KArgs& p, const GemmArgs& g, float scale_mode_ten
 }
 
 template <int FA, int FB>
-hipError_t gemm_fmt(const KArgs& p, int grid, bool e8m0, hipStream_t stream)
+hipError_t gemm_fmt(const KArgs& p, int grid, int mode, hipStream_t stream)
 {
-    if (e8m0)
-        hipLaunchKernelGGL((k_gemm_block<FA, FB, true>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+    if (mode == kModeE8M0)
+        hipLaunchKernelGGL((k_gemm_block<FA, FB, kModeE8M0>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+    else if (mode == kModeTensor)
+        hipLaunchKernelGGL((k_gemm_block<FA, FB, kModeTensor>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((k_gemm_block<FA, FB, false>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+        hipLaunchKernelGGL((k_gemm_block<FA, FB, kModeBlock>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -584,7 +598,12 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         if (p.splits == 1) p.ws = nullptr;
     }
     hipError_t e;
-    if (!g.block_scaled) {
+    // Per-tensor scales: the persistent kernel, except for a K split over
+    // 128-deep blocks, where the 8-wave kernel of the block-scaled form runs
+    // with per-tensor scales (one workgroup per tile and split, so there is no
+    // persistence to lose; measured 14% faster on 3072x768x65536).
+    const bool tensor_via_block = !g.block_scaled && p.ws && g.k % BK == 0;
+    if (!g.block_scaled && !tensor_via_block) {
         e = launch_gemm_persistent(g, gemm_num_cus(), stream);
         if (e != hipSuccess || !p.ws) return e;
         return launch_reduce(p, g, 1.0f, stream);
@@ -594,11 +613,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
     else
         p.fast_store = (g.n % 4 == 0) && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
-    const bool e8m0 = g.pow2_scales;
+    const int mode = !g.block_scaled ? kModeTensor : g.pow2_scales ? kModeE8M0 : kModeBlock;
     if (g.fa == FP8_E4M3)
-        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, grid, e8m0, stream) : gemm_fmt<0, 1>(p, grid, e8m0, stream);
+        e = g.fb == FP8_E4M3 ? gemm_fmt<0, 0>(p, grid, mode, stream) : gemm_fmt<0, 1>(p, grid, mode, stream);
     else
-        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, grid, e8m0, stream) : gemm_fmt<1, 1>(p, grid, e8m0, stream);
+        e = g.fb == FP8_E4M3 ? gemm_fmt<1, 0>(p, grid, mode, stream) : gemm_fmt<1, 1>(p, grid, mode, stream);
     if (e != hipSuccess || !p.ws) return e;
     return launch_reduce(p, g, g.block_scaled ? 0.0f : 1.0f, stream);
 }
