@@ -84,6 +84,23 @@ def test_split_k_and_determinism():
     assert_gemm_close(y, oracle.gemm(a, 0, sa, 1, b, 0, sb, 2), "block split-K")
 
 
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("m,n,k", [(300, 256, 4096), (257, 130, 4160), (64, 384, 8192)])
+def test_tensor_scaled_split_k_formats(fa, fb, m, n, k):
+    """Per-tensor GEMMs that split K, every format pair: K a multiple of 128
+    runs the 8-wave block kernel with per-tensor scales, K = 4160 the
+    persistent kernel's own split; both against the oracle, and a second call
+    bit-identical."""
+    g = np.random.default_rng(m + 3 * n + 7 * k + 11 * fa + 13 * fb)
+    a, sa = _codes(fa, g, (m, k), 0.05)
+    b, sb = _codes(fb, g, (n, k), 0.05)
+    assert fm.lib().fp8_scaled_mm_workspace_size(m, n, k, 0, 0) > 0
+    y1 = _run(a, fa, sa, 0, b, fb, sb, 0)
+    y2 = _run(a, fa, sa, 0, b, fb, sb, 0)
+    assert np.array_equal(y1, y2), "split-K result not deterministic"
+    assert_gemm_close(y1, oracle.gemm(a, fa, sa, 0, b, fb, sb, 0), f"split-K {fa}x{fb} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("n,ld_out", [(250, 250), (252, 260), (252, 254)])
 def test_split_k_reduction_layouts(n, ld_out):
     """Split-K outputs through both reductions: four outputs per thread
