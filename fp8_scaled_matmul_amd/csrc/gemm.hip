@@ -14,9 +14,10 @@
 //     VGPRs and the promotion is one v_fmac per output and K block, with no
 //     AGPR copies; two waves share each SIMD, so one wave's promotion FMAs
 //     run while the other's MFMAs occupy the matrix core;
-//   - one v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) covers exactly
-//     one K block of a 16x16 tile; its result is promoted three MFMAs later,
-//     when it is written;
+//   - one v_mfma_f32_16x16x128_f8f6f4 covers exactly one K block of a 16x16
+//     tile; its result is promoted three MFMAs later, when it is written (the
+//     power-of-two form uses v_mfma_scale_f32_16x16x128_f8f6f4 and needs no
+//     promotion);
 //   - A and B K blocks (2 x 32 KB) are double buffered in LDS, filled by
 //     buffer_load ... lds DMA: B early in the block two K blocks ahead, A
 //     after the block's last A read; s_a arrives by DMA two K blocks ahead and
