@@ -77,10 +77,9 @@ struct KArgs {
 // Map a linear workgroup id to (split, tile_m, tile_n).  Hardware hands ids
 // to XCDs round robin; re-number so that XCD x owns a contiguous block of
 // logical ids, then walk tiles M-grouped (kGroupM tile rows at a time).
-__device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn)
+__device__ inline void item_of(const KArgs& p, int bid, int& split, int& tm, int& tn)
 {
     const int total = p.tiles_m * p.tiles_n * p.splits;
-    const int bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3;
     const int q = total >> 3, rem = total & 7;
     const int pid = xcd * q + min(xcd, rem) + local;
@@ -95,6 +94,8 @@ __device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn)
     tm = first_m + r % gsize;
     tn = r / gsize;
 }
+
+__device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn) { item_of(p, blockIdx.x, split, tm, tn); }
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_a[2 * kTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
@@ -175,8 +176,9 @@ __device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w, bool
 // s_b pair).  `live` false turns the instruction into a
 // no-op fill (a zero-length descriptor: every lane reads as zero) so that
 // the K loop needs no branches past the end of the K range.
-__device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb, int kbs, bool live)
+__device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb, int kbs, bool live, int slot = -1)
 {
+    if (slot < 0) slot = kbs;
     const uint32_t k0 = (uint32_t)kb * BK;
     if (j < 4) {
         v4u r = d.ra;
@@ -190,10 +192,10 @@ __device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb
     } else {
         v4u r = d.rs;
         r.z = live ? r.z : 0u;
-        gemm::dma4(d.lds_s + (kbs & 3) * BM * 4, d.vs + (uint32_t)kbs * 4u, r);
+        gemm::dma4(d.lds_s + (slot & 3) * BM * 4, d.vs + (uint32_t)kbs * 4u, r);
         v4u rb = d.rsb;
         rb.z = live ? rb.z : 0u;
-        gemm::dma4(d.lds_sb + (kbs & 3) * 256, d.vsb + (uint32_t)kbs * 4u, rb);
+        gemm::dma4(d.lds_sb + (slot & 3) * 256, d.vsb + (uint32_t)kbs * 4u, rb);
     }
 }
 
@@ -448,6 +450,292 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
 }
 
+// Position in a workgroup's stream of K blocks: the persistent form walks the
+// items (tile, K split) blockIdx.x, blockIdx.x + gridDim.x, ... and the K
+// blocks of each.  All fields are uniform over the workgroup.
+struct BlockPos {
+    int id;         // item id; >= the item count once the stream has ended
+    int t;          // K block within the item
+    int kt0, ntk;   // the item's first K block and block count
+    int m0, n0, split;
+};
+
+__device__ inline void pos_load(const KArgs& p, BlockPos& q, int id)
+{
+    const int total = p.tiles_m * p.tiles_n * p.splits;
+    q.id = id;
+    q.t = 0;
+    if (id < total) {
+        int split, tm, tn;
+        item_of(p, id, split, tm, tn);
+        const int kt_per = (p.ktiles + p.splits - 1) / p.splits;
+        q.split = split;
+        q.kt0 = split * kt_per;
+        q.ntk = min(p.ktiles, q.kt0 + kt_per) - q.kt0;
+        q.m0 = tm * BM;
+        q.n0 = tn * BN;
+    } else {
+        q.split = 0;
+        q.kt0 = 0;
+        q.ntk = 1;
+        q.m0 = 0;
+        q.n0 = 0;
+    }
+}
+
+// Next K block; true when the position moved to another item.
+__device__ inline bool pos_next(const KArgs& p, BlockPos& q)
+{
+    if (++q.t < q.ntk) return false;
+    pos_load(p, q, q.id + (int)gridDim.x);
+    return true;
+}
+
+// The DMA descriptors of one item (uniform): A and B panels, and, for block
+// scales, s_a's rows and s_b (zero length for per-tensor scales).
+struct ItemDesc {
+    v4u ra, rb, rs, rsb;
+    int n0;
+};
+
+__device__ inline ItemDesc item_desc(const KArgs& p, const BlockPos& q, bool block_scales)
+{
+    ItemDesc e;
+    const int64_t rows_a = min(p.m - q.m0, BM), rows_b = min(p.n - q.n0, BN);
+    const int nkb = p.k / BK;
+    const int nbs = (p.n + 127) / 128;
+    e.ra = gemm::make_rsrc(p.a + (int64_t)q.m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    e.rb = gemm::make_rsrc(p.b + (int64_t)q.n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+    e.rs = gemm::make_rsrc(p.sa + (int64_t)q.m0 * nkb, block_scales ? (uint32_t)(rows_a * nkb * 4) : 0u);
+    e.rsb = gemm::make_rsrc(p.sb, block_scales ? (uint32_t)(nbs * nkb * 4) : 0u);
+    e.n0 = q.n0;
+    return e;
+}
+
+// A/B instruction j (0..7) of K block kb of an item into `stage`; lane
+// offsets and LDS targets from the workgroup's BlockDma.
+__device__ inline void item_dma_ab(const BlockDma& d, const ItemDesc& e, int j, int stage, int kb, bool live)
+{
+    const uint32_t k0 = (uint32_t)kb * BK;
+    if (j < 4) {
+        v4u r = e.ra;
+        r.z = live ? r.z : 0u;
+        dma16_so(d.lds_a + stage * kTileBytes + 1024 * j, d.va[j & 1], r, k0 + (uint32_t)(j >> 1) * d.step_a);
+    } else {
+        const int jb = j - 4;
+        v4u r = e.rb;
+        r.z = live ? r.z : 0u;
+        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, d.vb[jb & 1], r, k0 + (uint32_t)(jb >> 1) * d.step_b);
+    }
+}
+
+// s_a of K block kb and the item's two s_b values into ring slot `slot`.
+__device__ inline void item_dma_scales(const KArgs& p, const BlockDma& d, const ItemDesc& e, int slot, int kb, bool live)
+{
+    const int l = threadIdx.x & 63;
+    const int nkb = p.k / BK;
+    v4u r = e.rs;
+    r.z = live ? r.z : 0u;
+    gemm::dma4(d.lds_s + (slot & 3) * BM * 4, d.vs + (uint32_t)kb * 4u, r);
+    v4u rb = e.rsb;
+    rb.z = live ? rb.z : 0u;
+    const uint32_t vsb = l < 2 ? (uint32_t)(((e.n0 >> 7) + l) * nkb * 4 + kb * 4) : gemm::kOutOfRange;
+    gemm::dma4(d.lds_sb + (slot & 3) * 256, vsb, rb);
+}
+
+// Persistent form of k_gemm_block: the same K-block schedule, but over the
+// whole stream of the workgroup's items, so the DMA of the next tile's first
+// blocks runs during the current tile's last blocks and its epilogue.  LDS
+// stages and rings are indexed by the position u in the stream; one DMA
+// cursor runs two positions ahead, fetching each position's scales (slot 2)
+// before its B half (slots 2-5) and A half (slots 26-27).  Launched only
+// when every output row segment can be stored whole (fast_store).
+template <int FA, int FB, int MODE>
+__global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
+{
+    constexpr bool E8M0 = MODE == kModeE8M0;
+    constexpr bool TENSOR = MODE == kModeTensor;
+    constexpr bool PROMOTE = MODE == kModeBlock;
+    const float out_scale = (TENSOR && !p.ws) ? p.sa[0] * p.sb[0] : 1.0f;
+    const int total = p.tiles_m * p.tiles_n * p.splits;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wm = (wave & 1) * 128;
+    const int wn = (wave >> 1) * 64;
+    const int fcol = (wn >> 7) * BM + wm + 4 * (lane >> 4);
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    BlockPos c;
+    pos_load(p, c, blockIdx.x);
+    BlockPos da = c;     // DMA position, two blocks ahead of c
+    const BlockDma dl = block_dma(p, 0, 0, wave, false);   // lane offsets and LDS targets only
+    ItemDesc de = item_desc(p, da, !TENSOR);
+    // prologue: scales and A/B of positions 0 and 1
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        item_dma_scales(p, dl, de, u, da.kt0 + da.t, da.id < total);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) item_dma_ab(dl, de, j, u, da.kt0 + da.t, da.id < total);
+        if (pos_next(p, da)) de = item_desc(p, da, !TENSOR);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    gemm::barrier_lds();
+    if constexpr (E8M0) {
+        block_codes(0, wave);
+        block_codes(1, wave);
+    } else if constexpr (PROMOTE) {
+        block_factors(0, wave);
+        block_factors(1, wave);
+    }
+    gemm::barrier_lds();
+
+    v8i af[2], bf[4];
+    v4f fc[2], part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = gemm::load_frag(g_lds_b, wn + 16 * j);
+    af[0] = gemm::load_frag(g_lds_a, wm);
+    fc[0] = *reinterpret_cast<const v4f*>(&g_lds_f[fcol]);
+    fc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ecol = (wm >> 7) * 16 + (lane & 15);
+    const int nbi_w = wn >> 7;
+    uint2 ec = uint2{0, 0}, ecn = uint2{0, 0};
+    uint32_t bc = 0, bcn = 0;
+    if constexpr (E8M0) {
+        ec = *reinterpret_cast<const uint2*>(&g_lds_e[ecol * 8]);
+        bc = (__builtin_bit_cast(uint32_t, g_lds_sb[nbi_w]) >> 23) & 0xFFu;
+    }
+
+    uint32_t nonfinite = 0;
+    for (int u = 0; c.id < total; ++u) {
+        const uint8_t* la = g_lds_a + (u & 1) * kTileBytes;
+        const uint8_t* la_next = g_lds_a + ((u + 1) & 1) * kTileBytes;
+        const uint8_t* lb_next = g_lds_b + ((u + 1) & 1) * kTileBytes;
+        const float* lf = g_lds_f + (u & 3) * 2 * BM + fcol;
+        const float* lf_next = g_lds_f + ((u + 1) & 3) * 2 * BM + fcol;
+        const bool live2 = da.id < total;
+        const int kb2 = da.kt0 + da.t;
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+            const int i = s >> 2, j = s & 3;
+            if (j == 0) af[(i + 1) & 1] = gemm::load_frag(i < 7 ? la : la_next, i < 7 ? wm + 16 * (i + 1) : wm);
+            if constexpr (E8M0) {
+                acc[i][j] = mfma_e8m0<FA, FB>(i & 3, af[i & 1], bf[j], acc[i][j], i < 4 ? ec.x : ec.y, bc);
+                if (s == 31) {
+                    ecn = *reinterpret_cast<const uint2*>(&g_lds_e[((u + 1) & 3) * 256 + ecol * 8]);
+                    bcn = (__builtin_bit_cast(uint32_t, g_lds_sb[((u + 1) & 3) * 64 + nbi_w]) >> 23) & 0xFFu;
+                }
+            } else if constexpr (TENSOR) {
+                acc[i][j] = gemm::mfma<FA, FB>(af[i & 1], bf[j], acc[i][j]);
+            } else {
+                part[s & 3] = gemm::mfma<FA, FB>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            }
+            if constexpr (PROMOTE) {
+                const int q = (s + 32 - kLag) & 31, iq = q >> 2, jq = q & 3;
+                const v4f pr = part[(s + 4 - kLag) & 3];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[iq][jq][r] = __builtin_fmaf(pr[r], fc[iq & 1][r], acc[iq][jq][r]);
+            }
+            if (PROMOTE && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
+            if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
+            if (s == 1) gemm::barrier_lds();
+            if (s == 2) item_dma_scales(p, dl, de, u + 2, kb2, live2);
+            if (s >= 2 && s <= 5) item_dma_ab(dl, de, 4 + (s - 2), u & 1, kb2, live2);
+            if (s == 26) {
+                // all but this block's 4 B instructions (loads complete in order;
+                // an epilogue's stores before them are waited for too)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                gemm::barrier_lds();
+            }
+            if (s >= 26 && s <= 27) {
+                item_dma_ab(dl, de, 2 * (s - 26), u & 1, kb2, live2);
+                item_dma_ab(dl, de, 2 * (s - 26) + 1, u & 1, kb2, live2);
+            }
+            if (s == 27) {
+                if constexpr (E8M0)
+                    block_codes(u + 2, wave);
+                else if constexpr (PROMOTE)
+                    block_factors(u + 2, wave);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (E8M0) {
+            ec = ecn;
+            bc = bcn;
+        }
+        if (pos_next(p, da)) de = item_desc(p, da, !TENSOR);
+        if (c.t + 1 < c.ntk) {
+            ++c.t;
+            continue;
+        }
+        // the item's last block: its last kLag promotions, then the epilogue
+#pragma unroll
+        for (int s = 0; s < (PROMOTE ? kLag : 0); ++s) {
+            const int q = 32 - kLag + s, jq = q & 3;
+            const v4f pr = part[(s + 4 - kLag) & 3];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[7][jq][r] = __builtin_fmaf(pr[r], fc[1][r], acc[7][jq][r]);
+        }
+        // lane holds columns n0 + wn + 4 (lane%16) + j of rows m0 + wm + 16 i + 4 (lane/16) + r
+        const int m0 = c.m0, n0 = c.n0;
+        const int col = n0 + wn + 4 * (lane & 15);
+        const bool col_ok = col < p.n;
+        const int64_t rows_c = min(p.m - m0, BM);
+        if (p.ws) {
+            // fp32 partials: range-checked 16-byte stores
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                p.ws + ((int64_t)c.split * p.m + m0) * p.n, (short)0, (int)(rows_c * p.n * 4), 0x00020000);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
+                    const uint32_t off = col_ok ? (uint32_t)((lrow * p.n + col) * 4) : gemm::kOutOfRange;
+                    const v4f v = v4f{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rw, (int)off, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        } else {
+            const __amdgpu_buffer_rsrc_t rc =
+                __builtin_amdgcn_make_buffer_rsrc(p.c + (int64_t)m0 * p.ldc, (short)0,
+                                                  (int)std::min<int64_t>(rows_c * p.ldc * 2, 0x7FFFFFF0), 0x00020000);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
+                    const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * out_scale, acc[i][1][r] * out_scale);
+                    const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * out_scale, acc[i][3][r] * out_scale);
+                    const bool in = col_ok && m0 + lrow < p.m;
+                    nonfinite += in ? (((lo & 0x7F80u) == 0x7F80u) + ((lo & 0x7F800000u) == 0x7F800000u) +
+                                       ((hi & 0x7F80u) == 0x7F80u) + ((hi & 0x7F800000u) == 0x7F800000u))
+                                    : 0u;
+                    const uint32_t off = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : gemm::kOutOfRange;
+                    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                    __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 2);   // nontemporal
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        // the next block's first kLag slots promote zeros (finite factors)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        fc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        pos_next(p, c);
+    }
+    flush_counters(p.ctr, 0, 0, 0, nonfinite);
+}
+
 // Fixed-order reduction of split-K partials: y = bf16(scale * sum_s ws[s]).
 __global__ void __launch_bounds__(256) k_splitk_reduce(const float* ws, int splits, int m, int n, float scale_mode_tensor,
                                                        const float* sa, const float* sb, uint16_t* c, int64_t ldc,
@@ -527,6 +815,15 @@ hipError_t launch_reduce(const KArgs& p, const GemmArgs& g, float scale_mode_ten
 template <int FA, int FB>
 hipError_t gemm_fmt(const KArgs& p, int grid, int mode, hipStream_t stream)
 {
+    // per-tensor scales with whole row segments and more tiles than CUs: the
+    // persistent form (its epilogue stays within the register budget only in
+    // this mode; with one tile per workgroup it only adds cursor work: 2%
+    // slower on 3072x768x65536 split 7 ways)
+    if (p.fast_store && mode == kModeTensor && grid > gemm_num_cus()) {
+        const int g = std::min(grid, gemm_num_cus());
+        hipLaunchKernelGGL((k_gemm_block_p<FA, FB, kModeTensor>), dim3(g), dim3(kBlockThreads), 0, stream, p);
+        return hipGetLastError();
+    }
     if (mode == kModeE8M0)
         hipLaunchKernelGGL((k_gemm_block<FA, FB, kModeE8M0>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     else if (mode == kModeTensor)
@@ -599,11 +896,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         if (p.splits == 1) p.ws = nullptr;
     }
     hipError_t e;
-    // Per-tensor scales: the persistent kernel, except for a K split over
-    // 128-deep blocks, where the 8-wave kernel of the block-scaled form runs
-    // with per-tensor scales (one workgroup per tile and split, so there is no
-    // persistence to lose; measured 14% faster on 3072x768x65536).
-    const bool tensor_via_block = !g.block_scaled && p.ws && g.k % BK == 0;
+    // Per-tensor scales: the 8-wave kernel of the block-scaled form (with
+    // per-tensor scales, persistent over tiles) when K is a multiple of 128 and
+    // either split or at least 16 blocks deep; else the 4-wave persistent
+    // kernel.  Measured in the step: 3072x768x65536 (split) 14% and
+    // 65536x768x3072 3% faster on the 8-wave kernel, 65536x3072x768 (6 blocks
+    // per tile) 2% slower.
+    const bool tensor_via_block = !g.block_scaled && g.k % BK == 0 && (p.ws || g.k >= 16 * BK);
     if (!g.block_scaled && !tensor_via_block) {
         e = launch_gemm_persistent(g, gemm_num_cus(), stream);
         if (e != hipSuccess || !p.ws) return e;
@@ -611,7 +910,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
     }
     const int grid = p.tiles_m * p.tiles_n * p.splits;
     if (p.ws)
-        p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0);
+        p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0) &&
+                       (int64_t)BM * g.n * 4 < 0x7FFFFFF0;   // a tile's rows of partials fit one descriptor
     else
         p.fast_store = (g.n % 4 == 0) && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
     const int mode = !g.block_scaled ? kModeTensor : g.pow2_scales ? kModeE8M0 : kModeBlock;

@@ -101,6 +101,20 @@ def test_tensor_scaled_split_k_formats(fa, fb, m, n, k):
     assert_gemm_close(y1, oracle.gemm(a, fa, sa, 0, b, fb, sb, 0), f"split-K {fa}x{fb} {m}x{n}x{k}")
 
 
+def test_tensor_scaled_persistent_block_kernel():
+    """A per-tensor GEMM with K = 2048 (16 blocks) and 288 output tiles: the
+    8-wave kernel runs persistent, some workgroups take two tiles, the second
+    one's first K blocks fetched during the first one's last blocks.  Sampled
+    outputs, whole last row and column, against the oracle."""
+    g = np.random.default_rng(77)
+    m, n, k = 4608, 4096, 2048
+    a, sa = _codes(fm.E5M2, g, (m, k), 0.05)
+    b, sb = _codes(fm.E4M3, g, (n, k), 0.05)
+    assert fm.lib().fp8_scaled_mm_workspace_size(m, n, k, 0, 0) == 0
+    y = host(fm.scaled_mm(dev_u8(a), fm.E5M2, dev_f32(sa), 0, dev_u8(b), fm.E4M3, dev_f32(sb), 0))
+    _check_points(y, a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0, g, "persistent 4608x4096x2048")
+
+
 @pytest.mark.parametrize("n,ld_out", [(250, 250), (252, 260), (252, 254)])
 def test_split_k_reduction_layouts(n, ld_out):
     """Split-K outputs through both reductions: four outputs per thread
