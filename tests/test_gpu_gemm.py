@@ -115,6 +115,21 @@ def test_tensor_scaled_persistent_block_kernel():
     _check_points(y, a, fm.E5M2, sa, 0, b, fm.E4M3, sb, 0, g, "persistent 4608x4096x2048")
 
 
+@pytest.mark.parametrize("fa,fb,m,n", [(fm.E4M3, fm.E4M3, 4500, 4100), (fm.E4M3, fm.E5M2, 4500, 4100),
+                                         (fm.E5M2, fm.E4M3, 4400, 4098)])
+def test_tensor_scaled_deep_k_ragged(fa, fb, m, n):
+    """K = 2048 with ragged M and N and more than 256 tiles: the persistent
+    8-wave kernel (N % 4 == 0, partial edge tiles on both sides) and the
+    single-tile kernel's element stores (N = 4098).  Sampled outputs plus
+    whole last row and column against the oracle."""
+    g = np.random.default_rng(m + n + fa + 3 * fb)
+    k = 2048
+    a, sa = _codes(fa, g, (m, k), 0.05)
+    b, sb = _codes(fb, g, (n, k), 0.05)
+    y = host(fm.scaled_mm(dev_u8(a), fa, dev_f32(sa), 0, dev_u8(b), fb, dev_f32(sb), 0))
+    _check_points(y, a, fa, sa, 0, b, fb, sb, 0, g, f"deep K {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("n,ld_out", [(250, 250), (252, 260), (252, 254)])
 def test_split_k_reduction_layouts(n, ld_out):
     """Split-K outputs through both reductions: four outputs per thread
