@@ -290,7 +290,7 @@ def main():
 KERNEL_SOURCES = {
     "gemm_block_16384x2048x7168": ["gemm.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
     "gemm_fwd_65536x3072x768": ["gemm_persistent.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
-    "gemm_dx_65536x768x3072": ["gemm_persistent.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
+    "gemm_dx_65536x768x3072": ["gemm.hip", "gemm_common.h", "device_common.h", "fp8mi_internal.h"],
 }
 
 
