@@ -260,11 +260,13 @@ def test_backward_workload_sampled():
     assert np.array_equal(h_dyq, odq) and host(dys)[0] == ods[0]
 
 
-@pytest.mark.parametrize("block", [False, True])
-def test_largest_leading_dimensions(block):
+@pytest.mark.parametrize("block,k", [(False, 256), (True, 256), (False, 2048)])
+def test_largest_leading_dimensions(block, k):
     """lda, ldb just below 2^22 and ldc just below 2^21 (the limits the C ABI
-    accepts): the 32-bit offsets inside a tile reach their largest values."""
-    m, n, k = 256, 384, 256
+    accepts): the 32-bit offsets inside a tile reach their largest values.
+    Per-tensor scales with K = 256 run the 4-wave kernel, with K = 2048 the
+    8-wave kernel with per-tensor scales."""
+    m, n = 256, 384
     lda = ldb = (1 << 22) - 16
     ldc = (1 << 21) - 8
     g = np.random.default_rng(71)
