@@ -45,7 +45,6 @@ using gemm::v8i;
 using gemm::BM;
 using gemm::BN;
 using gemm::BK;
-using gemm::kGroupM;
 using gemm::kTileBytes;
 
 constexpr int kBlockThreads = 512;
@@ -71,12 +70,13 @@ struct KArgs {
     int ktiles;          // ceil(k / BK)
     int tiles_m, tiles_n;
     int fast_store;      // 8-byte bf16 (16-byte fp32) stores are aligned
+    int group_m;         // M tiles per group of the tile order
     fp8_counters* ctr;
 };
 
 // Map a linear workgroup id to (split, tile_m, tile_n).  Hardware hands ids
 // to XCDs round robin; re-number so that XCD x owns a contiguous block of
-// logical ids, then walk tiles M-grouped (kGroupM tile rows at a time).
+// logical ids, then walk tiles M-grouped (p.group_m tile rows at a time).
 __device__ inline void item_of(const KArgs& p, int bid, int& split, int& tm, int& tn)
 {
     const int total = p.tiles_m * p.tiles_n * p.splits;
@@ -86,10 +86,10 @@ __device__ inline void item_of(const KArgs& p, int bid, int& split, int& tm, int
     const int per_split = p.tiles_m * p.tiles_n;
     split = pid / per_split;
     const int t = pid - split * per_split;
-    const int in_group = kGroupM * p.tiles_n;
+    const int in_group = p.group_m * p.tiles_n;
     const int g = t / in_group;
-    const int first_m = g * kGroupM;
-    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int first_m = g * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
     const int r = t - g * in_group;
     tm = first_m + r % gsize;
     tn = r / gsize;
@@ -909,6 +909,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
         return launch_reduce(p, g, 1.0f, stream);
     }
     const int grid = p.tiles_m * p.tiles_n * p.splits;
+    // M tiles per group of the tile order, measured per kernel form in the
+    // step: 4 for the single-tile form (block-scaled 16384x2048x7168 1.3%
+    // faster than 8), 8 for the persistent per-tensor form (65536x768x3072 3%
+    // faster than 4); 2 and 16 were no better
+    p.group_m = (tensor_via_block && grid > gemm_num_cus()) ? 8 : 4;
     if (p.ws)
         p.fast_store = (g.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.ws) & 15u) == 0) &&
                        (int64_t)BM * g.n * 4 < 0x7FFFFFF0;   // a tile's rows of partials fit one descriptor

@@ -19,7 +19,6 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kTileBytes = BM * BK;     // 32 KB: one operand tile of one K step
-constexpr int kGroupM = 8;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // 16-byte chunk c (0..7) of the 128-byte LDS row r lives at chunk position

@@ -65,6 +65,7 @@ struct PArgs {
     int tiles_m, tiles_n;
     int items, per_xcd, g8;
     int fast_store;     // row-segment stores are aligned and in range
+    int group_m;        // M tiles per group of the tile order
     fp8_counters* ctr;
 };
 
@@ -122,10 +123,10 @@ __device__ inline Item decode_item(const PArgs& p, int item)
     Item it;
     it.split = item / per_split;
     const int t = item - it.split * per_split;
-    const int in_group = kGroupM * p.tiles_n;
+    const int in_group = p.group_m * p.tiles_n;
     const int g = t / in_group;
-    const int first_m = g * kGroupM;
-    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int first_m = g * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
     const int r = t - g * in_group;
     // all of it is uniform over the workgroup: keep it in scalar registers
     it.m0 = __builtin_amdgcn_readfirstlane((first_m + r % gsize) * BM);
@@ -532,6 +533,9 @@ hipError_t launch_gemm_persistent(const GemmArgs& g, int num_cus, hipStream_t st
     p.ws = splits > 1 ? g.ws : nullptr;
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
+    // M tiles per group of the tile order (65536x3072x768: 4.5% faster with 4
+    // than with 8; 2 and 16 no better)
+    p.group_m = 4;
     p.items = p.tiles_m * p.tiles_n * p.splits;
     const int max_g8 = std::max(1, num_cus / 8);
     int grid;
