@@ -1,0 +1,73 @@
+"""Seeded random-shape parity sweep of the scaled GEMM against the fp64
+oracle, to the same tolerance as the fixed-shape tests (max|y - y_ref| <=
+1e-2 max|y_ref|, relative Frobenius <= 5e-3).  The shapes are drawn once from
+a fixed seed: m and n anywhere from 1 to a few tiles (ragged in both), k any
+multiple of 16 (per-tensor) or of 128 (block-scaled), and short outputs over
+deep K so that the split-K forms and both per-tensor kernels are reached.
+Each case prints its shape in the assertion message."""
+import numpy as np
+import pytest
+
+import fp8_scaled_matmul_amd as fm
+import oracle
+import synth
+from gpu_util import assert_gemm_close, dev_f32, dev_u8, host
+
+pytestmark = pytest.mark.gpu
+PAIRS = [(fm.E4M3, fm.E4M3), (fm.E5M2, fm.E4M3), (fm.E4M3, fm.E5M2), (fm.E5M2, fm.E5M2)]
+
+
+def _tensor_cases():
+    g = np.random.default_rng(20240611)
+    out = []
+    for i in range(24):
+        if i % 3 == 2:     # short output, deep K
+            m, n, k = int(g.integers(1, 300)), int(g.integers(1, 300)), 16 * int(g.integers(128, 384))
+        else:
+            m, n, k = int(g.integers(1, 700)), int(g.integers(1, 700)), 16 * int(g.integers(1, 96))
+        out.append((i, m, n, k))
+    return out
+
+
+def _block_cases():
+    g = np.random.default_rng(20240612)
+    out = []
+    for i in range(12):
+        if i % 3 == 2:
+            m, n, k = int(g.integers(1, 260)), int(g.integers(1, 260)), 128 * int(g.integers(16, 40))
+        else:
+            m, n, k = int(g.integers(1, 700)), int(g.integers(1, 700)), 128 * int(g.integers(1, 10))
+        out.append((i, m, n, k))
+    return out
+
+
+def _codes(fmt, seed, shape, sigma):
+    v = synth.normal_bf16(seed, 0, shape, sigma)
+    q, _, s, _ = oracle.quantize(v, fmt)
+    return q, s
+
+
+@pytest.mark.parametrize("i,m,n,k", _tensor_cases())
+def test_tensor_scaled_random_shapes(i, m, n, k):
+    fa, fb = PAIRS[i % 4]
+    a, sa = _codes(fa, 1000 + i, (m, k), 1.0)
+    b, sb = _codes(fb, 2000 + i, (n, k), 0.02)
+    y = fm.scaled_mm(dev_u8(a), fa, dev_f32(np.float32(sa).reshape(1)), fm.TENSOR,
+                     dev_u8(b), fb, dev_f32(np.float32(sb).reshape(1)), fm.TENSOR)
+    ref = oracle.gemm(a, fa, sa, oracle.TENSOR, b, fb, sb, oracle.TENSOR)
+    assert_gemm_close(host(y), ref, f"tensor case {i}: {m}x{n}x{k} formats {fa},{fb}")
+
+
+@pytest.mark.parametrize("i,m,n,k", _block_cases())
+def test_block_scaled_random_shapes(i, m, n, k):
+    fa, fb = PAIRS[i % 2]
+    pow2 = i % 4 == 3
+    quant = oracle.quantize_pow2 if pow2 else oracle.quantize
+    av = synth.channel_scaled_bf16(300 + i, 0, 3, (m, k))
+    bv = synth.channel_scaled_bf16(300 + i, 1, 4, (n, k))
+    a, _, sa, _ = quant(av, fa, oracle.ROW_1x128)
+    b, _, sb, _ = quant(bv, fb, oracle.BLOCK_128x128)
+    ga, gb = (fm.ROW_1x128_POW2, fm.BLOCK_128x128_POW2) if pow2 else (fm.ROW_1x128, fm.BLOCK_128x128)
+    y = fm.scaled_mm(dev_u8(a), fa, dev_f32(sa.reshape(-1)), ga, dev_u8(b), fb, dev_f32(sb.reshape(-1)), gb)
+    ref = oracle.gemm(a, fa, sa, oracle.ROW_1x128, b, fb, sb, oracle.BLOCK_128x128)
+    assert_gemm_close(host(y), ref, f"block case {i}: {m}x{n}x{k} formats {fa},{fb} pow2={pow2}")
