@@ -4,7 +4,8 @@ oracle, to the same tolerance as the fixed-shape tests (max|y - y_ref| <=
 a fixed seed: m and n anywhere from 1 to a few tiles (ragged in both), k any
 multiple of 16 (per-tensor) or of 128 (block-scaled), and short outputs over
 deep K so that the split-K forms and both per-tensor kernels are reached.
-Each case prints its shape in the assertion message."""
+The quantizers get the same treatment, bit-exact.  Each case prints its
+shape in the assertion message."""
 import numpy as np
 import pytest
 
@@ -71,3 +72,32 @@ def test_block_scaled_random_shapes(i, m, n, k):
     y = fm.scaled_mm(dev_u8(a), fa, dev_f32(sa.reshape(-1)), ga, dev_u8(b), fb, dev_f32(sb.reshape(-1)), gb)
     ref = oracle.gemm(a, fa, sa, oracle.ROW_1x128, b, fb, sb, oracle.BLOCK_128x128)
     assert_gemm_close(host(y), ref, f"block case {i}: {m}x{n}x{k} formats {fa},{fb} pow2={pow2}")
+
+
+# ------------------------------------------------------------------ quantizers
+from gpu_util import dev_bf16, gpu_quantize, same_counters  # noqa: E402
+
+
+def _quant_cases():
+    g = np.random.default_rng(20240613)
+    out = [(i, int(g.integers(1, 700)), int(g.integers(1, 1100))) for i in range(14)]
+    # two larger ones: whole tiles over more than one round of workgroups, plus edges
+    return out + [(14, 4100, 3000), (15, 5000, 4500)]
+
+
+@pytest.mark.parametrize("i,rows,cols", _quant_cases())
+def test_quantize_random_shapes(i, rows, cols):
+    """Bytes, transposed bytes, scales and counters bit-exact for per-tensor
+    (with and without the transposed copy), 1x128 and 128x128 scales."""
+    fmt = (fm.E4M3, fm.E5M2)[i % 2]
+    x = synth.channel_scaled_bf16(400 + i, 0, 5, (rows, cols))
+    xd = dev_bf16(x)
+    for gran, want_t in ((fm.TENSOR, False), (fm.TENSOR, True), (fm.ROW_1x128, False), (fm.BLOCK_128x128, True)):
+        q, qt, s, c = gpu_quantize(xd, fmt, gran, fm.FROM_AMAX, None, want_t)
+        oq, oqt, os_, oc = oracle.quantize(x, fmt, gran, oracle.FROM_AMAX, None, want_t)
+        what = f"case {i}: {rows}x{cols} format {fmt} granularity {gran} transposed {want_t}"
+        assert np.array_equal(s.reshape(os_.shape), os_), f"{what}: scales differ"
+        assert np.array_equal(q, oq), f"{what}: {int((q != oq).sum())} codes differ"
+        if want_t:
+            assert np.array_equal(qt, oqt), f"{what}: transposed codes differ"
+        assert same_counters(c, oc), f"{what}: counters gpu {c} oracle {oc}"
