@@ -55,8 +55,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU share is "
-              "the whole workload; see DESIGN.md for how it would shard). Run with --gpus 1.",
+        print("bench.py measures one GPU: the path has no multi-GPU form (one GPU's share is the "
+              "whole workload). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
