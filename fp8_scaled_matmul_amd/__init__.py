@@ -175,9 +175,56 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _check_2d(t, name):
-    if t.dim() != 2 or t.stride(1) != 1:
+# Host-side checks of every tensor handed to the C ABI.  The library sees raw
+# device pointers and cannot tell an undersized, mistyped or host-resident
+# buffer from a good one, so the binding checks dtype, shape, strides and
+# device before anything is enqueued, and raises ValueError on a mismatch.
+# Shape and dtype checks come first; the device check (CUDA, one device for
+# all tensors of a call) last.
+def _check_tensor(t, name, dtypes, shape=None, contiguous=False, unit_col_stride=False):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if unit_col_stride and (t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1)):
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+
+
+def _check_scale(t, name, gran, rows, cols):
+    torch = _torch()
+    want = scale_shape(gran, rows, cols)
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be torch.float32, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() != int(_prod(want)):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {int(_prod(want))} elements "
+                         f"(shape {want} for this granularity), got shape {tuple(t.shape)}")
+
+
+def _prod(shape):
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def _check_devices(*tensors):
+    """Every tensor given is on one CUDA device."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"tensors must be on a CUDA (HIP) device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors of one call must share a device ({dev} vs {t.device})")
 
 
 def scale_shape(gran: int, rows: int, cols: int) -> tuple[int, ...]:
@@ -211,7 +258,8 @@ class Counters:
 
 def amax(x, gran: int = TENSOR):
     torch = _torch()
-    _check_2d(x, "x")
+    _check_tensor(x, "x", (torch.bfloat16, torch.float32), unit_col_stride=True)
+    _check_devices(x)
     rows, cols = x.shape
     out = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
     wsb = lib().fp8_amax_workspace_size(rows, cols, gran)
@@ -225,11 +273,21 @@ def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scal
              want_t: bool = False, counters: Counters | None = None, out=None, out_t=None):
     """Returns (q uint8 [rows, cols], q_t uint8 [cols, rows] or None, scale fp32)."""
     torch = _torch()
-    _check_2d(x, "x")
+    _check_tensor(x, "x", (torch.bfloat16, torch.float32), unit_col_stride=True)
     rows, cols = x.shape
     if scale is None:
         if mode == GIVEN:
             raise ValueError("GIVEN mode needs a scale tensor")
+    else:
+        _check_scale(scale, "scale", gran, rows, cols)
+    if out is not None:
+        _check_tensor(out, "out", (torch.uint8,), (rows, cols), unit_col_stride=True)
+    if want_t and out_t is not None:
+        _check_tensor(out_t, "out_t", (torch.uint8,), (cols, rows), unit_col_stride=True)
+    if out_t is not None and not want_t:
+        raise ValueError("out_t given without want_t=True")
+    _check_devices(x, scale, out, out_t, counters.buf if counters else None)
+    if scale is None:
         scale = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
     q = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     qt = None
@@ -261,8 +319,22 @@ def quantize_delayed(x, fmt: int, history: AmaxHistory, scale=None, want_t: bool
     """Per-tensor quantize with the scale of the recorded amax history, then
     record this tensor's amax.  Returns (q, q_t or None, scale)."""
     torch = _torch()
-    _check_2d(x, "x")
+    _check_tensor(x, "x", (torch.bfloat16, torch.float32), unit_col_stride=True)
     rows, cols = x.shape
+    if scale is not None:
+        _check_scale(scale, "scale", TENSOR, rows, cols)
+    if out is not None:
+        _check_tensor(out, "out", (torch.uint8,), (rows, cols), unit_col_stride=True)
+    if want_t and out_t is not None:
+        _check_tensor(out_t, "out_t", (torch.uint8,), (cols, rows), unit_col_stride=True)
+    if out_t is not None and not want_t:
+        raise ValueError("out_t given without want_t=True")
+    _check_tensor(history.values, "history.values", (torch.float32,), (history.length,), contiguous=True)
+    _check_tensor(history.pos, "history.pos", (torch.int32,), (1,), contiguous=True)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", (torch.uint8,), contiguous=True)
+    _check_devices(x, scale, out, out_t, history.values, history.pos, workspace,
+                   counters.buf if counters else None)
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=x.device)
     q = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
@@ -285,12 +357,21 @@ def scaled_mm(a, fa: int, scale_a, ga: int, b, fb: int, scale_b, gb: int,
               out=None, counters: Counters | None = None, workspace=None):
     """y = (s_a A)(s_b B)^T, a [m,k] uint8, b [n,k] uint8 -> bf16 [m,n]."""
     torch = _torch()
-    _check_2d(a, "a")
-    _check_2d(b, "b")
+    _check_tensor(a, "a", (torch.uint8,), unit_col_stride=True)
+    _check_tensor(b, "b", (torch.uint8,), unit_col_stride=True)
     m, k = a.shape
     n, k2 = b.shape
     if k != k2:
         raise ValueError("a and b disagree on k")
+    if ga not in (TENSOR, ROW_1x128, ROW_1x128_POW2) or gb not in (TENSOR, BLOCK_128x128, BLOCK_128x128_POW2):
+        raise ValueError("scale_a is TENSOR or ROW_1x128(_POW2), scale_b TENSOR or BLOCK_128x128(_POW2)")
+    _check_scale(scale_a, "scale_a", ga, m, k)
+    _check_scale(scale_b, "scale_b", gb, n, k)
+    if out is not None:
+        _check_tensor(out, "out", (torch.bfloat16,), (m, n), unit_col_stride=True)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", (torch.uint8,), contiguous=True)
+    _check_devices(a, b, scale_a, scale_b, out, workspace, counters.buf if counters else None)
     c = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     wsb = lib().fp8_scaled_mm_workspace_size(m, n, k, ga, gb)
     if workspace is None and wsb:
@@ -329,6 +410,11 @@ def requant_weights(caches: list[WeightCache], masters: list) -> None:
     torch = _torch()
     if not caches:
         return
+    if len(caches) != len(masters):
+        raise ValueError("one master per cache")
+    for c, m in zip(caches, masters):
+        _check_tensor(m, "master", (torch.bfloat16, torch.float32), (c.rows, c.cols), contiguous=True)
+    _check_devices(*masters, *[c.q for c in caches])
     descs = [c.desc() for c in caches]
     arr = (WeightCacheDesc * len(descs))(*descs)
     wsb = lib().fp8_requant_workspace_size(arr, len(descs))

@@ -119,17 +119,3 @@ def test_gemm_pow2_extreme_scales():
         b, _, sb, _ = oracle.quantize_pow2(bv, fm.E4M3, oracle.BLOCK_128x128)
         y, _ = _gemm_pow2(a, 0, sa, b, 0, sb)
         assert_gemm_close(y, oracle.gemm(a, 0, sa, 1, b, 0, sb, 2), f"pow2 sigma {sigma}")
-
-
-def test_gemm_pow2_workload_sampled():
-    a = synth.channel_scaled_bf16(4, 0, 3, synth.BLOCK_SCALED["a"])
-    b = synth.channel_scaled_bf16(4, 1, 4, synth.BLOCK_SCALED["b"])
-    aq, _, sa = fm.quantize(dev_bf16(a), fm.E4M3, fm.ROW_1x128, fm.FROM_AMAX_POW2)
-    bq, _, sb = fm.quantize(dev_bf16(b), fm.E4M3, fm.BLOCK_128x128, fm.FROM_AMAX_POW2)
-    y = host(fm.scaled_mm(aq, 0, sa, fm.ROW_1x128_POW2, bq, 0, sb, fm.BLOCK_128x128_POW2))
-    g = np.random.default_rng(44)
-    m, n = y.shape
-    pm = np.concatenate([g.integers(0, m, 3000), np.full(n, 12345), np.arange(m) % m])
-    pn = np.concatenate([g.integers(0, n, 3000), np.arange(n), np.full(m, 1023)])
-    ref = oracle.gemm_points(host(aq), 0, host(sa), 1, host(bq), 0, host(sb), 2, pm, pn)
-    assert_gemm_close(y[pm, pn], ref, "pow2 block-scaled 16384")
