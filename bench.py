@@ -9,13 +9,19 @@ tokens plus a fine-grained block-scaled projection:
   backward  quantize dY [65536,3072] -> E5M2 (per-tensor, + dY^T copy)
             dX = dY W             [65536,768]    (E5M2 x E4M3, W^T cache copy)
             dW = dY^T X           [3072,768]     (K = 65536, split K)
-  update    optimizer-side master change, then the weight-cache refresh
-            (amax + cast + transposed copy of W [3072,768])
+  update    the weight-cache refresh after the optimizer step (amax + cast +
+            transposed copy of W [3072,768]); the step alternates between the
+            master before and after one update W <- bf16(W + N(0,1e-4)),
+            both prepared beforehand, so every refresh sees a changed master
   fine      quantize A [16384,7168] in 1x128 row tiles, B [2048,7168] in
             128x128 blocks, block-scaled GEMM [16384,2048]
 
 value = all GEMM flops of the step / step time (TFLOP/s, inputs resident in
-HBM).  A breakdown pass before the timed region brackets every stage with
+HBM).  Outside the timed region, the other workloads are measured too: the
+256x3072x768 up-projection (one call and a loop of 1000 calls), the 8192 x
+8192 quantize-only pass (amax, per-tensor and 1x128 quantize in E4M3 and
+E5M2, the 256 MB last-level cache flushed before every rep), and the batched
+refresh of a 12-layer model's up-projection caches.  A breakdown pass before the timed region brackets every stage with
 HIP events (each stage's average duration); the timed region records events
 only around the dominant kernel, whose average launch duration gives the
 roofline entry.  The CPU oracle is timed on a bounded sample of the same
@@ -75,11 +81,13 @@ def main():
     t_gen = time.time()
     x = to_dev(synth.normal_bf16(3, 0, (TOK, D), 1.0))
     w_bits = synth.normal_bf16(3, 1, (F, D), 0.02)
-    w_master = to_dev(w_bits)
+    # the master before and after one optimizer update (the step refreshes
+    # the cache from each in turn)
+    w_masters = [to_dev(w_bits), to_dev(synth.apply_update_bf16(w_bits, synth.update_noise_f32(3, (F, D))))]
+    w_master = w_masters[0]
     dy = to_dev(synth.normal_bf16(5, 0, (TOK, F), 1e-3))
     a_fine = to_dev(synth.channel_scaled_bf16(4, 0, 3, (FA_M, FA_K)))
     b_fine = to_dev(synth.channel_scaled_bf16(4, 1, 4, (FA_N, FA_K)))
-    noise = torch.from_numpy(synth.update_noise_f32(3, (F, D))).to(dev)
     gen_s = time.time() - t_gen
 
     # outputs and caches, allocated once
@@ -122,6 +130,12 @@ def main():
     del csrc, cdst
     torch.cuda.synchronize()
 
+    refresh_state = [0]
+
+    def refresh(c):
+        fm.requant_weights([c], [w_masters[refresh_state[0] & 1]])
+        refresh_state[0] += 1
+
     # (name, flops, algorithmic HBM bytes, callable)
     stages = [
         ("quantize_x_e4m3_tensor_t", 0, TOK * D * (2 + 2 + 1 + 1),
@@ -138,7 +152,7 @@ def main():
          lambda: fm.scaled_mm(dyqt, fm.E5M2, dys, fm.TENSOR, xqt, fm.E4M3, xs, fm.TENSOR,
                               out=dw, counters=ctr, workspace=dw_ws)),
         ("requant_w_cache", 0, F * D * (2 + 2 + 1 + 1),
-         lambda: fm.requant_weights([cache], [w_master])),
+         lambda: refresh(cache)),
         ("quantize_a_1x128", 0, FA_M * FA_K * 3 + FA_M * (FA_K // 128) * 4,
          lambda: fm.quantize(a_fine, fm.E4M3, fm.ROW_1x128, scale=sa, out=aq, counters=ctr)),
         ("quantize_b_128x128", 0, FA_N * FA_K * 3 + (FA_N // 128) * (FA_K // 128) * 4,
@@ -176,8 +190,6 @@ def main():
     ]
 
     def step(dom_events=None, dom=None):
-        # the optimizer's master update precedes the cache refresh (not timed
-        # as part of the FP8 path: it is the caller's optimizer)
         for name, _, _, fn in stages:
             timed = dom_events is not None and name == dom
             if timed:
@@ -248,6 +260,7 @@ def main():
     counters = ctr.read()
     value = step_flops / (ms_per_step / 1e3) / 1e12
     bf16 = bf16_matched(torch, x, w_master, dy, stage_ms, args.steps)
+    other = other_workloads(torch, fm, synth, np, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -280,9 +293,160 @@ def main():
         "counters": counters,
         "hbm_copy_gbs": round(copy_gbs, 1),
         "bf16_matched": bf16,
+        "workloads": other,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out))
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def _rate(nbytes, ms):
+    return {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+            "frac_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def other_workloads(torch, fm, synth, np, dev):
+    """The workloads that are not part of the training step, each timed on its
+    own with HIP events on the current stream (outside the timed region):
+
+    - the 256x3072x768 up-projection (X [256,768] N(0,1), W [3072,768]
+      N(0,0.02), E4M3 per-tensor): median of 50 single calls of each stage,
+      and the average over a loop of 1000 calls (quantize X, quantize W,
+      GEMM) -- a latency-bound shape (12 output tiles for 256 CUs);
+    - the quantize-only pass over bf16 [8192,8192] N(0,1) with 0.1% outliers
+      +-U(500,5000): amax (2 B/elt), per-tensor quantize from amax (two
+      kernels: 3 B/elt useful, 5 B/elt moved), per-tensor cast with a given
+      scale (3 B/elt), 1x128 tile quantize (3 + 4/128 B/elt), in E4M3 and
+      E5M2; before every rep a 1 GiB buffer is read so that the input is not
+      served from the 256 MB last-level cache; median of 15 reps;
+    - the weight-cache refresh of a 12-layer model's up-projection weights
+      (12 x [3072,768] bf16 -> E4M3 per-tensor with transposed copies; 6 B
+      per element algorithmic), one batched call against 12 single calls."""
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def time_calls(fn, reps, flush=None):
+        out = []
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return out
+
+    res = {}
+    # ---- 256x3072x768 up-projection
+    x1 = to_dev(synth.normal_bf16(1, 0, synth.SMALL_UP_PROJ["x"], 1.0))
+    w1 = to_dev(synth.normal_bf16(1, 1, synth.SMALL_UP_PROJ["w"], 0.02))
+    m, k = x1.shape
+    n = w1.shape[0]
+    xq1 = torch.empty((m, k), dtype=torch.uint8, device=dev)
+    wq1 = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    xs1 = torch.empty(1, dtype=torch.float32, device=dev)
+    ws1 = torch.empty(1, dtype=torch.float32, device=dev)
+    y1 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    fq_x = lambda: fm.quantize(x1, fm.E4M3, scale=xs1, out=xq1)
+    fq_w = lambda: fm.quantize(w1, fm.E4M3, scale=ws1, out=wq1)
+    fg = lambda: fm.scaled_mm(xq1, fm.E4M3, xs1, fm.TENSOR, wq1, fm.E4M3, ws1, fm.TENSOR, out=y1)
+    for _ in range(20):
+        fq_x(), fq_w(), fg()
+    torch.cuda.synchronize()
+    flops1 = 2 * m * n * k
+    single = {name: _median(time_calls(fn, 50)) for name, fn in
+              (("quantize_x", fq_x), ("quantize_w", fq_w), ("gemm", fg))}
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(1000):
+        fg()
+    b.record()
+    torch.cuda.synchronize()
+    loop_gemm = a.elapsed_time(b) / 1000
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(1000):
+        fq_x(), fq_w(), fg()
+    b.record()
+    torch.cuda.synchronize()
+    loop_all = a.elapsed_time(b) / 1000
+    res["up_projection_256x3072x768"] = {
+        "single_call_us": {k_: round(v * 1e3, 2) for k_, v in single.items()},
+        "gemm_tflops_single": round(flops1 / single["gemm"] / 1e9, 1),
+        "loop_1000_gemm_us": round(loop_gemm * 1e3, 2),
+        "loop_1000_gemm_tflops": round(flops1 / loop_gemm / 1e9, 1),
+        "loop_1000_quantize_x_w_gemm_us": round(loop_all * 1e3, 2),
+    }
+    del x1, w1, xq1, wq1, y1
+
+    # ---- 8192 x 8192 quantize-only
+    shp = synth.QUANT_ONLY["x"]
+    xq_in = to_dev(synth.with_outliers_bf16(2, shp))
+    nel = shp[0] * shp[1]
+    q8 = torch.empty(shp, dtype=torch.uint8, device=dev)
+    s_t = torch.empty(1, dtype=torch.float32, device=dev)
+    s_r = torch.empty((shp[0], shp[1] // 128), dtype=torch.float32, device=dev)
+    amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_a = torch.empty(fm.lib().fp8_amax_workspace_size(shp[0], shp[1], fm.TENSOR), dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        # read 1 GiB (no dirty lines left behind to be written back while the
+        # timed kernel runs)
+        flush_buf.sum()
+
+    cases = [("amax", 2 * nel, None, lambda: fm.check(fm.fp8_amax(
+        xq_in.data_ptr(), fm.BF16, shp[0], shp[1], shp[1], fm.TENSOR, amax_out.data_ptr(), ws_a.data_ptr(),
+        ws_a.numel(), torch.cuda.current_stream().cuda_stream)))]
+    for fmt, fname in ((fm.E4M3, "e4m3"), (fm.E5M2, "e5m2")):
+        cases += [
+            (f"quantize_tensor_{fname}", 3 * nel, 5 * nel,
+             lambda fmt=fmt: fm.quantize(xq_in, fmt, fm.TENSOR, scale=s_t, out=q8)),
+            (f"cast_given_scale_{fname}", 3 * nel, None,
+             lambda fmt=fmt: fm.quantize(xq_in, fmt, fm.TENSOR, fm.GIVEN, scale=s_t, out=q8)),
+            (f"quantize_1x128_{fname}", 3 * nel + 4 * nel // 128, None,
+             lambda fmt=fmt: fm.quantize(xq_in, fmt, fm.ROW_1x128, scale=s_r, out=q8)),
+        ]
+    qo = {}
+    for name, useful, moved, fn in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = _median(time_calls(fn, 15, flush))
+        d = _rate(useful, ms)
+        if moved:
+            d["gbs_moved"] = round(moved / ms / 1e6, 1)
+            d["frac_hbm_moved"] = round(moved / ms / 1e6 / PEAK_HBM_GBS, 4)
+        qo[name] = d
+    res["quantize_only_8192x8192"] = qo
+    del xq_in, q8, s_r, flush_buf
+
+    # ---- 12-layer weight-cache refresh
+    wl = [to_dev(synth.normal_bf16(70 + l, 1, (3072, 768), 0.02)) for l in range(12)]
+    caches = [fm.WeightCache(3072, 768, with_t=True, device=dev) for _ in wl]
+    batched = lambda: fm.requant_weights(caches, wl)
+
+    def singles():
+        for c, w in zip(caches, wl):
+            fm.requant_weights([c], [w])
+    for _ in range(3):
+        batched(), singles()
+    torch.cuda.synchronize()
+    nbytes = 12 * 3072 * 768 * 6
+    res["requant_12_layers_3072x768"] = {
+        "batched": _rate(nbytes, _median(time_calls(batched, 30))),
+        "twelve_single_calls": _rate(nbytes, _median(time_calls(singles, 30))),
+    }
+    return res
 
 
 # Sources each GEMM kernel is compiled from; a stored traffic figure is used

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "fp8mi.h"
 #include "fp8mi_internal.h"
@@ -329,6 +330,8 @@ fp8_status fp8_requant_weights(const fp8_weight_cache* caches, const void* const
         const fp8_weight_cache& c = caches[i];
         if (c.gran != FP8_TENSOR && c.gran != FP8_BLOCK_128x128)
             return fail(FP8_ERR_UNSUPPORTED_SHAPE, "weight caches use TENSOR or BLOCK_128x128 scaling");
+        if (c.rows >= ((int64_t)1 << 31) || c.cols >= ((int64_t)1 << 31))
+            return fail(FP8_ERR_UNSUPPORTED_SHAPE, "weight cache rows and cols must be below 2^31");
         fp8_status s = check_quantize_args(masters[i], master_dtypes[i], c.rows, c.cols, c.cols, c.fmt, c.gran,
                                            FP8_SCALE_FROM_AMAX, c.scale, c.q, c.cols, c.q_t, c.rows,
                                            c.gran == FP8_TENSOR ? workspace : nullptr,
@@ -338,9 +341,10 @@ fp8_status fp8_requant_weights(const fp8_weight_cache* caches, const void* const
     fp8_status s = check_device();
     if (s != FP8_OK) return s;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    std::vector<QuantArgs> args((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
         const fp8_weight_cache& c = caches[i];
-        QuantArgs a;
+        QuantArgs& a = args[(size_t)i];
         a.x = masters[i];
         a.dtype = master_dtypes[i];
         a.rows = c.rows;
@@ -360,10 +364,9 @@ fp8_status fp8_requant_weights(const fp8_weight_cache* caches, const void* const
             a.partials = reinterpret_cast<uint32_t*>(ws);
             ws += kAmaxWorkspaceBytes;
         }
-        hipError_t e = launch_quantize(a, stream);
-        if (e != hipSuccess) return hip_fail(e, "fp8_requant_weights launch");
     }
-    return FP8_OK;
+    hipError_t e = launch_requant(args.data(), count, stream);
+    return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_requant_weights launch");
 }
 
 fp8_status fp8_counters_reset(fp8_counters* ctr, hipStream_t stream)

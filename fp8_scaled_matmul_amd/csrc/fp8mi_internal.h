@@ -32,6 +32,29 @@ struct QuantArgs {
     int pow2 = 0;       // FROM_AMAX with the power-of-two scale rule
 };
 
+// One weight cache of a batched refresh, as the kernels see it (kernel
+// argument; all pointers device pointers).
+struct RequantItem {
+    const void* x;          // master [rows, cols], contiguous
+    uint8_t* q;             // [rows, cols]
+    uint8_t* qt;            // [cols, rows] or null
+    float* scale;
+    fp8_counters* ctr;      // nullable
+    uint32_t* parts;        // per-tensor: this cache's partial keys
+    int64_t tile0;          // first 128x128 tile of this cache in the batch's tile list
+    int32_t rows, cols;
+    int32_t wg0, nwg;       // per-tensor: its amax workgroups (one partial key each)
+    int8_t dtype, fmt, gran;
+    int8_t vec_amax, vec_tile;
+};
+constexpr int kRequantMaxCaches = 24;    // caches per launch (kernel-argument size)
+constexpr int kRequantAmaxParts = 256;   // at most this many partial keys per cache
+struct RequantBatch {
+    int32_t count;
+    int64_t total_tiles;
+    RequantItem item[kRequantMaxCaches];
+};
+
 // Each launcher enqueues on `stream` and returns the hipError_t of the launch.
 hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                               float* out, uint32_t* partials, hipStream_t stream);
@@ -40,6 +63,8 @@ hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t c
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos, int len, hipStream_t stream);
 hipError_t launch_counters_reset(fp8_counters* ctr, hipStream_t stream);
+// Every cache's QuantArgs (FROM_AMAX; per-tensor ones with their partials).
+hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream);
 
 struct GemmArgs {
     const uint8_t* a;

@@ -338,40 +338,24 @@ __global__ void __launch_bounds__(kThreads) k_cast_tensor(const void* x, int64_t
 constexpr int kTile = 128;
 constexpr int kTilePitch = kTile + 8;   // bytes per LDS row
 
+// One 128x128 tile (tile index tid of the tensor's row-major tile grid).
+// s_tensor / special_tensor / from_partials describe the per-tensor scale
+// (SCALE_MODE 0); the per-block modes derive or read their own.  `tile` is
+// the workgroup's LDS staging area for the transposed copy.
 template <int FMT, int DT, int SCALE_MODE, bool AMAX_ONLY>
-__global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t rows, int64_t cols,
-                                                      int64_t ld, int vec, float* scale,
-                                                      const uint32_t* partials, int np, uint8_t* q,
-                                                      int64_t ldq, uint8_t* qt, int64_t ldqt,
-                                                      fp8_counters* ctr, int only_partial, int pow2)
+__device__ inline void tile128_one(const void* x, int64_t rows, int64_t cols, int64_t ld, int vec, float* scale,
+                                   float s_tensor, bool special_tensor, bool from_partials, uint8_t* q, int64_t ldq,
+                                   uint8_t* qt, int64_t ldqt, int pow2, int64_t tid, uint8_t* tile,
+                                   uint32_t& sat, uint32_t& und, uint32_t& nan)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTilePitch];
     const int t = threadIdx.x;
     const int cc = (t & 15) * 8;
     const int rr = t >> 4;
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
-    const int64_t tiles_r = (rows + kTile - 1) / kTile;
-    const int64_t ntiles = tiles_r * tiles_c;
-
-    float s_tensor = 1.0f;
-    bool special_tensor = true;
-    if constexpr (SCALE_MODE == 0) {
-        if (partials) {
-            const uint32_t k = reduce_partials(partials, np);
-            special_tensor = key_special(k);
-            s_tensor = scale_rule<FMT>(key_amax(k), pow2);
-            if (blockIdx.x == 0 && t == 0) scale[0] = s_tensor;
-        } else {
-            s_tensor = scale[0];
-        }
-    }
-    uint32_t sat = 0, und = 0, nan = 0;
-
-    for (int64_t tid = blockIdx.x; tid < ntiles; tid += gridDim.x) {
+    {
         const int64_t r0 = (tid / tiles_c) * kTile;
         const int64_t c0 = (tid % tiles_c) * kTile;
         const bool full = vec && r0 + kTile <= rows && c0 + kTile <= cols;
-        if (only_partial && r0 + kTile <= rows && c0 + kTile <= cols) continue;   // done by k_tile128_bf16
         float xv[8][8];
         uint32_t key = 0;
         if (full) {
@@ -390,13 +374,13 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
         bool fast;
         if constexpr (SCALE_MODE == 0) {
             s = s_tensor;
-            fast = DT == 0 && partials && !special_tensor && s >= kCorrectedQuotMinScale;
+            fast = DT == 0 && from_partials && !special_tensor && s >= kCorrectedQuotMinScale;
         } else if constexpr (SCALE_MODE == 1) {
             key = block_key_merge(key);
             const int64_t sidx = (r0 / kTile) * tiles_c + c0 / kTile;
             if constexpr (AMAX_ONLY) {
                 if (t == 0) scale[sidx] = key_amax(key);
-                continue;
+                return;
             }
             s = scale_rule<FMT>(key_amax(key), pow2);
             if (t == 0) scale[sidx] = s;
@@ -469,6 +453,41 @@ __global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t row
             }
             __syncthreads();
         }
+    }
+}
+
+// One workgroup per 128x128 tile, grid-strided over the tile grid.
+template <int FMT, int DT, int SCALE_MODE, bool AMAX_ONLY>
+__global__ void __launch_bounds__(kThreads) k_tile128(const void* x, int64_t rows, int64_t cols,
+                                                      int64_t ld, int vec, float* scale,
+                                                      const uint32_t* partials, int np, uint8_t* q,
+                                                      int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                                      fp8_counters* ctr, int only_partial, int pow2)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTilePitch];
+    const int64_t tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t tiles_r = (rows + kTile - 1) / kTile;
+    const int64_t ntiles = tiles_r * tiles_c;
+
+    float s_tensor = 1.0f;
+    bool special_tensor = true;
+    if constexpr (SCALE_MODE == 0) {
+        if (partials) {
+            const uint32_t k = reduce_partials(partials, np);
+            special_tensor = key_special(k);
+            s_tensor = scale_rule<FMT>(key_amax(k), pow2);
+            if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s_tensor;
+        } else {
+            s_tensor = scale[0];
+        }
+    }
+    uint32_t sat = 0, und = 0, nan = 0;
+    for (int64_t tid = blockIdx.x; tid < ntiles; tid += gridDim.x) {
+        const int64_t r0 = (tid / tiles_c) * kTile, c0 = (tid % tiles_c) * kTile;
+        if (only_partial && r0 + kTile <= rows && c0 + kTile <= cols) continue;   // done by k_tile128_bf16
+        tile128_one<FMT, DT, SCALE_MODE, AMAX_ONLY>(x, rows, cols, ld, vec, scale, s_tensor, special_tensor,
+                                                    partials != nullptr, q, ldq, qt, ldqt, pow2, tid, tile, sat, und,
+                                                    nan);
     }
     if constexpr (!AMAX_ONLY) flush_counters_block(ctr, sat, und, nan);
 }
@@ -873,6 +892,133 @@ __global__ void __launch_bounds__(kThreads) k_row1x128(const void* x, int64_t ro
     if constexpr (!AMAX_ONLY) flush_counters_block(ctr, sat, und, nan);
 }
 
+// ------------------------------------------------------------------ weight-cache refresh, batched
+// The refresh of many caches in two launches ("#84 FP8 Precision", section
+// "Hardware precision": after each optimizer step the master weights are
+// quantized again into their FP8 copies).  k_requant_amax reduces every
+// per-tensor cache's master to partial keys (each cache owns a contiguous
+// run of workgroups and its own partial array); k_requant_cast then walks the
+// 128x128 tiles of all caches, per-tensor ones scaled from their partials,
+// per-block ones from each block's own amax, with the same tile code as
+// k_tile128.  The caches of one launch travel in the kernel arguments.
+
+// max |x| key over the elements [b, e) of a contiguous tensor (16-byte
+// vectors when vec and b is a multiple of 8); the whole workgroup calls it.
+template <int DT>
+__device__ inline uint32_t amax_range(const void* x, int64_t b, int64_t e, bool vec)
+{
+    constexpr int per_vec = DT == 0 ? 8 : 4;
+    const int64_t nv = vec ? (e - b) / per_vec : 0;
+    const int64_t tail0 = b + nv * per_vec;
+    uint32_t key = 0;
+    if constexpr (DT == 0) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        us2 pk = us2{0, 0};
+        for (int64_t v = threadIdx.x; v < nv; v += kThreads) pk = pkmax8(pk, ld_stream(xb + b + v * 8));
+        for (int64_t c = tail0 + threadIdx.x; c < e; c += kThreads) {
+            const uint32_t h = xb[c] & 0x7FFFu;
+            pk.x = pk.x > h ? pk.x : (unsigned short)h;
+        }
+        key = pk_raw(pk);
+        if (key >= kRawNonFinite) {
+            // an Inf or NaN in this thread's share: the exact, flag-carrying merge
+            key = 0;
+            for (int64_t v = threadIdx.x; v < nv; v += kThreads) {
+                const uint4 w = *reinterpret_cast<const uint4*>(xb + b + v * 8);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    key = key_merge(key, absbits_bf16(ws[h] & 0xFFFFu));
+                    key = key_merge(key, absbits_bf16(ws[h] >> 16));
+                }
+            }
+            for (int64_t c = tail0 + threadIdx.x; c < e; c += kThreads) key = key_merge(key, absbits_bf16(xb[c]));
+        }
+    } else {
+        const uint32_t* xb = static_cast<const uint32_t*>(x);
+        for (int64_t v = threadIdx.x; v < nv; v += kThreads) {
+            const uint4 w = ld_stream(xb + b + v * 4);
+            key = key_merge(key, absbits_f32(w.x));
+            key = key_merge(key, absbits_f32(w.y));
+            key = key_merge(key, absbits_f32(w.z));
+            key = key_merge(key, absbits_f32(w.w));
+        }
+        for (int64_t c = tail0 + threadIdx.x; c < e; c += kThreads) key = key_merge(key, absbits_f32(xb[c]));
+    }
+    return block_key_merge(key);
+}
+
+__global__ void __launch_bounds__(kThreads) k_requant_amax(RequantBatch bt)
+{
+    const int bid = blockIdx.x;
+    int c = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (bt.item[i].nwg > 0 && bid >= bt.item[i].wg0) c = i;
+    const RequantItem& it = bt.item[c];
+    const int local = bid - it.wg0;
+    if (it.nwg == 0 || local < 0 || local >= it.nwg) return;   // (never: the grid is the sum of nwg)
+    const int64_t n = (int64_t)it.rows * it.cols;
+    const int64_t per = ((n + it.nwg - 1) / it.nwg + 7) & ~(int64_t)7;
+    const int64_t b = min(n, (int64_t)local * per), e = min(n, b + per);
+    const uint32_t key = it.dtype == FP8_IN_BF16 ? amax_range<0>(it.x, b, e, it.vec_amax)
+                                                 : amax_range<1>(it.x, b, e, it.vec_amax);
+    if (threadIdx.x == 0) it.parts[local] = key;
+}
+
+template <int FMT, int DT>
+__device__ inline void requant_tile(const RequantItem& it, float s, bool special, int64_t tid, uint8_t* tile,
+                                    uint32_t& sat, uint32_t& und, uint32_t& nan)
+{
+    if (it.gran == FP8_TENSOR)
+        tile128_one<FMT, DT, 0, false>(it.x, it.rows, it.cols, it.cols, it.vec_tile, it.scale, s, special, true, it.q,
+                                       it.cols, it.qt, it.rows, 0, tid, tile, sat, und, nan);
+    else
+        tile128_one<FMT, DT, 1, false>(it.x, it.rows, it.cols, it.cols, it.vec_tile, it.scale, 1.0f, true, false,
+                                       it.q, it.cols, it.qt, it.rows, 0, tid, tile, sat, und, nan);
+}
+
+__global__ void __launch_bounds__(kThreads) k_requant_cast(RequantBatch bt)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTilePitch];
+    const int64_t per = (bt.total_tiles + gridDim.x - 1) / gridDim.x;
+    const int64_t t0 = (int64_t)blockIdx.x * per, t1 = min(bt.total_tiles, t0 + per);
+    int c = -1;
+    float s = 1.0f;
+    bool special = true;
+    uint32_t sat = 0, und = 0, nan = 0;
+    for (int64_t f = t0; f < t1; ++f) {
+        int cn = 0;
+        for (int i = 1; i < bt.count; ++i)
+            if (f >= bt.item[i].tile0) cn = i;
+        if (cn != c) {
+            if (c >= 0) {
+                flush_counters_block(bt.item[c].ctr, sat, und, nan);
+                __syncthreads();
+                sat = und = nan = 0;
+            }
+            c = cn;
+            const RequantItem& it = bt.item[c];
+            if (it.gran == FP8_TENSOR) {
+                const uint32_t k = reduce_partials(it.parts, it.nwg);
+                special = key_special(k);
+                s = it.fmt == FP8_E4M3 ? scale_from_amax<0>(key_amax(k)) : scale_from_amax<1>(key_amax(k));
+                if (f == it.tile0 && threadIdx.x == 0) it.scale[0] = s;
+            }
+        }
+        const RequantItem& it = bt.item[c];
+        const int64_t tid = f - it.tile0;
+        if (it.fmt == FP8_E4M3) {
+            if (it.dtype == FP8_IN_BF16) requant_tile<0, 0>(it, s, special, tid, tile, sat, und, nan);
+            else requant_tile<0, 1>(it, s, special, tid, tile, sat, und, nan);
+        } else {
+            if (it.dtype == FP8_IN_BF16) requant_tile<1, 0>(it, s, special, tid, tile, sat, und, nan);
+            else requant_tile<1, 1>(it, s, special, tid, tile, sat, und, nan);
+        }
+        __syncthreads();   // the LDS staging tile and the block amax scratch are reused by the next tile
+    }
+    if (c >= 0) flush_counters_block(bt.item[c].ctr, sat, und, nan);
+}
+
 __global__ void k_counters_reset(fp8_counters* ctr)
 {
     if (threadIdx.x < 4) reinterpret_cast<unsigned long long*>(ctr)[threadIdx.x] = 0ull;
@@ -1029,6 +1175,62 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)
     if (a.fmt == FP8_E4M3)
         return a.dtype == FP8_IN_BF16 ? quantize_typed<0, 0>(a, stream) : quantize_typed<0, 1>(a, stream);
     return a.dtype == FP8_IN_BF16 ? quantize_typed<1, 0>(a, stream) : quantize_typed<1, 1>(a, stream);
+}
+
+// Weight-cache refresh: the caches go in groups of kRequantMaxCaches; per
+// group one amax launch over its per-tensor caches (if any) and one cast
+// launch over all of its caches.  Empty caches take launch_quantize (a
+// per-tensor one still reports scale 1).
+hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream)
+{
+    hipError_t e;
+    for (int g0 = 0; g0 < count; g0 += kRequantMaxCaches) {
+        RequantBatch bt{};
+        int wg = 0;
+        int64_t tiles = 0;
+        for (int i = g0; i < std::min(count, g0 + kRequantMaxCaches); ++i) {
+            const QuantArgs& a = caches[i];
+            if (a.rows == 0 || a.cols == 0) {
+                if ((e = launch_quantize(a, stream)) != hipSuccess) return e;
+                continue;
+            }
+            RequantItem& it = bt.item[bt.count++];
+            const int eb = a.dtype == FP8_IN_BF16 ? 2 : 4;
+            it.x = a.x;
+            it.q = a.q;
+            it.qt = a.qt;
+            it.scale = a.scale;
+            it.ctr = a.ctr;
+            it.parts = a.partials;
+            it.rows = a.rows;
+            it.cols = a.cols;
+            it.dtype = (int8_t)a.dtype;
+            it.fmt = (int8_t)a.fmt;
+            it.gran = (int8_t)a.gran;
+            it.vec_amax = aligned16(a.x);
+            it.vec_tile = aligned16(a.x) && aligned16(a.q) && (!a.qt || aligned16(a.qt)) && (a.cols * eb) % 16 == 0 &&
+                          a.cols % 8 == 0 && (!a.qt || a.rows % 16 == 0);
+            it.tile0 = tiles;
+            tiles += cdiv(a.rows, kTile) * cdiv(a.cols, kTile);
+            it.wg0 = wg;
+            it.nwg = 0;
+            if (a.gran == FP8_TENSOR) {
+                const int64_t n = a.rows * a.cols;
+                it.nwg = (int)std::min<int64_t>(std::max<int64_t>(cdiv(n, (int64_t)kThreads * 64), 1), kRequantAmaxParts);
+                wg += it.nwg;
+            }
+        }
+        if (bt.count == 0) continue;
+        bt.total_tiles = tiles;
+        if (wg > 0) {
+            hipLaunchKernelGGL(k_requant_amax, dim3(wg), dim3(kThreads), 0, stream, bt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        const int grid = (int)std::min<int64_t>(tiles, (int64_t)num_cus() * 4);
+        hipLaunchKernelGGL(k_requant_cast, dim3(grid), dim3(kThreads), 0, stream, bt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Delayed scaling.  A bf16 tensor of whole 128x128 tiles with 16-byte rows

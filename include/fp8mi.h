@@ -65,8 +65,9 @@ typedef enum {
 } fp8_granularity;
 typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1, FP8_SCALE_FROM_AMAX_POW2 = 2 } fp8_scale_mode;
 
-/* Telemetry ("summary statistics of clipping and overflow events", NanoChat
- * FAQ; "overflow telemetry", guardrails explainer).  Lives in device memory;
+/* Telemetry: counts of clipping and overflow events (the NanoChat page's FAQ
+ * recommends logging them; the guardrails explainer lists overflow counters
+ * among its checks).  Lives in device memory;
  * every call that takes a non-NULL pointer ADDS its events with integer
  * atomics.  Reset with fp8_counters_reset().
  *   saturated     - elements whose value x/s, rounded to nearest-even on the
@@ -87,8 +88,9 @@ const char* fp8_status_string(fp8_status s);
 const char* fp8_last_error(void);
 
 /* ------------------------------------------------------------------ amax
- * max |x| over the finite elements of each scaling group ("measure each batch
- * ... pick padding", guardrails explainer; amax history, "Real products").
+ * max |x| over the finite elements of each scaling group (the guardrails
+ * explainer derives scales from the measured range of the data, and keeps an
+ * amax history in its section "Real products").
  *   x      [rows, cols], leading dimension ld >= cols, bf16 or fp32.
  *   amax   out: 1 float (TENSOR), [rows, ceil(cols/128)] (ROW_1x128) or
  *          [ceil(rows/128), ceil(cols/128)] (BLOCK_128x128), row-major.
@@ -105,9 +107,10 @@ fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, 
  * Scale, then cast: for each element of each scaling group
  *     v = fl32(x / s)                    (IEEE fp32 division, exactly rounded)
  *     q = round-to-nearest-even(v) on the format's grid, saturated to +-max
- * ("Weights are divided by a learned scale before quantizing", #84 lab card,
- * section "Explanation"; overflow saturates / tiny values underflow to zero,
- * guardrails explainer).  NaN -> 0x7F|sign, +-Inf -> +-max.
+ * (#84 lab card, section "Explanation": the weight is divided by its scale
+ * and then cast to FP8; the guardrails explainer: values past the format's
+ * maximum saturate and very small ones become zero).  NaN -> 0x7F|sign,
+ * +-Inf -> +-max.
  *   mode FROM_AMAX: s = fl32(amax / fmax) per group (fmax 448 or 57344);
  *       amax == 0 gives s = 1; s below FLT_MIN is raised to FLT_MIN.  The
  *       scales are WRITTEN to `scale`.
@@ -215,10 +218,10 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda,
                          fp8_counters* ctr, hipStream_t stream);
 
 /* ------------------------------------------------------------------ weight cache
- * The FP8 compute copy of master weights: "After each optimizer step, the
- * BF16 weights are re-quantized to FP8 and cached for the next forward pass"
- * (#84 lab card, "Hardware precision"; quantize_weights_fp8 in its second
- * code excerpt).  Each descriptor names caller-owned device storage:
+ * The FP8 compute copy of master weights, rebuilt from the bf16 master after
+ * every optimizer step and kept for the next forward pass (#84 lab card,
+ * "Hardware precision"; quantize_weights_fp8 in its second code excerpt).
+ * Each descriptor names caller-owned device storage:
  *   rows, cols  shape of the master [rows, cols] (contiguous, ld = cols);
  *   fmt, gran   format and granularity (TENSOR or BLOCK_128x128 here);
  *   q           [rows, cols] bytes; q_t optional [cols, rows] bytes (the
@@ -226,9 +229,13 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda,
  *   scale       1 float (TENSOR) or the block grid (BLOCK_128x128);
  *   ctr         optional counters.
  * fp8_requant_weights() re-quantizes every cache from its master with a
- * fresh amax scale (current scaling), in two launches for all TENSOR caches
- * (one amax pass, one cast pass) and one for all BLOCK caches.  The result is
- * byte-identical to fp8_quantize(master, FROM_AMAX) of each.  masters[i] is a
+ * fresh amax scale (current scaling).  The caches go in groups of up to 24;
+ * each group takes two launches: one amax pass over its TENSOR caches (left
+ * out when it has none) and one cast pass over all of its caches, TENSOR
+ * caches with the scale of their amax pass, BLOCK caches with each block's
+ * own amax.  An empty TENSOR cache gets scale 1 from a launch of its own.
+ * The result is byte-identical to fp8_quantize(master, FROM_AMAX) of each,
+ * counters included.  rows and cols below 2^31.  masters[i] is a
  * device pointer, master_dtypes[i] its dtype; the three arrays are HOST arrays
  * of length count.  Workspace: fp8_requant_workspace_size(). */
 typedef struct {

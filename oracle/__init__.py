@@ -235,9 +235,10 @@ def count_nonfinite_bf16(y: np.ndarray) -> int:
 
 def requant(master: np.ndarray, fmt: int, gran: int = TENSOR, want_t: bool = True):
     """The weight-copy cache refresh after an optimizer step ("#84 FP8
-    Precision", section "Hardware precision": the bf16 master is
-    re-quantized to FP8 and cached for the next forward).  By definition it
-    is a fresh quantize of the current master with a current amax scale."""
+    Precision", section "Hardware precision": the FP8 copy is rebuilt from the
+    bf16 master after every step and kept for the next forward pass).  By
+    definition it is a fresh quantize of the current master with a current
+    amax scale."""
     return quantize(master, fmt, gran, FROM_AMAX, None, want_t)
 
 

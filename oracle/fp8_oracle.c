@@ -129,8 +129,8 @@ static void count_event(orc_counters* c, int ev)
     else if (ev == ORC_EV_NAN) c->nan++;
 }
 
-/* "Weights are divided by a learned scale before quantizing" (#84 lab card,
- * section "Explanation"): the quotient is the IEEE fp32 one. */
+/* Division by the scale comes before the FP8 cast (#84 lab card, section
+ * "Explanation"); the quotient is the IEEE fp32 one. */
 uint8_t orc_cast_one(int fmt, float x, float s, orc_counters* ctr)
 {
     volatile float v = x / s;   /* one correctly rounded fp32 division */

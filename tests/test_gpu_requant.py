@@ -68,3 +68,90 @@ def test_cache_equals_quantize():
     fm.requant_weights([cache], [master])
     q, qt, s = fm.quantize(master, fm.E4M3, want_t=True)
     assert torch.equal(q, cache.q) and torch.equal(qt, cache.q_t) and torch.equal(s, cache.scale)
+
+
+def _mixed_cache_set(count, seed):
+    """`count` caches of mixed shape (whole and ragged 128x128 tiles, columns
+    not a multiple of 8), format, granularity, master dtype and transposed
+    copy, each with its own counters; an outlier in some masters so that
+    per-block scales differ from the per-tensor one."""
+    g = np.random.default_rng(seed)
+    base = [(3072, 768), (768, 3072), (200, 130), (128, 256), (257, 129), (64, 100), (1, 1), (130, 7),
+            (512, 640), (384, 128), (100, 300), (2304, 768)]
+    specs = []
+    for i in range(count):
+        shp = base[i % len(base)]
+        gran = fm.TENSOR if (i * 7) % 3 != 0 else fm.BLOCK_128x128
+        fmt = fm.E4M3 if i % 2 == 0 else fm.E5M2
+        fp32 = i % 5 == 3
+        with_t = i % 4 != 1
+        if fp32:
+            mval = (g.standard_normal(shp) * 0.05).astype(np.float32)
+            if i % 3 == 0 and mval.size > 1:
+                mval.reshape(-1)[g.integers(mval.size)] = 37.5
+        else:
+            mval = synth.normal_bf16(400 + seed * 64 + i, 1, shp, 0.02)
+            if i % 3 == 1 and mval.size > 1:
+                mval.reshape(-1)[g.integers(mval.size)] = 0x4300   # 128.0
+        specs.append((shp, gran, fmt, fp32, with_t, mval))
+    return specs
+
+
+@pytest.mark.parametrize("count", [17, 40])
+def test_batched_refresh_matches_oracle(count):
+    """One fp8_requant_weights call over many caches (17 fits one launch
+    group, 40 spans two): every cache's codes, transposed copy, scale(s) and
+    counters equal the oracle's requant of its master, bit for bit."""
+    specs = _mixed_cache_set(count, count)
+    caches, masters, ctrs, expect = [], [], [], []
+    for shp, gran, fmt, fp32, with_t, mval in specs:
+        ctr = fm.Counters()
+        masters.append(dev_f32(mval) if fp32 else dev_bf16(mval))
+        caches.append(fm.WeightCache(*shp, fmt=fmt, gran=gran, with_t=with_t, counters=ctr))
+        ctrs.append(ctr)
+        expect.append(oracle.requant(mval, fmt, gran, want_t=with_t))
+    fm.requant_weights(caches, masters)
+    for i, (c, ctr, (oq, oqt, os_, oc)) in enumerate(zip(caches, ctrs, expect)):
+        assert np.array_equal(host(c.q), oq), f"cache {i}: codes"
+        if c.q_t is not None:
+            assert np.array_equal(host(c.q_t), oqt), f"cache {i}: transposed codes"
+        assert np.array_equal(host(c.scale).reshape(os_.shape).view(np.uint32), os_.view(np.uint32)), \
+            f"cache {i}: scales"
+        got = ctr.read()
+        for f in ("saturated", "underflow", "nan"):
+            assert got[f] == oc[f], f"cache {i}: counter {f}"
+    # a second refresh of the same masters is idempotent
+    fm.requant_weights(caches, masters)
+    for i, (c, (oq, _, _, _)) in enumerate(zip(caches, expect)):
+        assert np.array_equal(host(c.q), oq), f"cache {i}: second refresh"
+
+
+def test_batched_refresh_empty_cache():
+    """An empty per-tensor cache among others reports scale 1 and leaves the
+    others intact."""
+    w = synth.normal_bf16(60, 1, (256, 384), 0.02)
+    empty = fm.WeightCache(0, 384, with_t=True)
+    empty.scale.fill_(7.0)
+    full = fm.WeightCache(256, 384, fmt=fm.E5M2, with_t=True)
+    fm.requant_weights([empty, full], [torch.empty((0, 384), dtype=torch.bfloat16, device="cuda"), dev_bf16(w)])
+    oq, oqt, os_, _ = oracle.requant(w, fm.E5M2)
+    assert host(empty.scale)[0] == 1.0
+    assert np.array_equal(host(full.q), oq) and np.array_equal(host(full.q_t), oqt) and host(full.scale)[0] == os_[0]
+
+
+def test_twelve_layer_refresh():
+    """The up-projection caches of a 12-layer model ([3072,768] E4M3, per
+    tensor, with transposed copies) refreshed in one call after an update of
+    every master."""
+    ws = [synth.normal_bf16(70 + l, 1, (3072, 768), 0.02) for l in range(12)]
+    caches = [fm.WeightCache(3072, 768, with_t=True) for _ in ws]
+    masters = [dev_bf16(w) for w in ws]
+    fm.requant_weights(caches, masters)
+    ws2 = [synth.apply_update_bf16(w, synth.update_noise_f32(70 + l, w.shape)) for l, w in enumerate(ws)]
+    for m, w2 in zip(masters, ws2):
+        m.copy_(dev_bf16(w2))
+    fm.requant_weights(caches, masters)
+    for l, (c, w2) in enumerate(zip(caches, ws2)):
+        oq, oqt, os_, _ = oracle.requant(w2, fm.E4M3)
+        assert np.array_equal(host(c.q), oq) and np.array_equal(host(c.q_t), oqt), f"layer {l}"
+        assert host(c.scale)[0] == os_[0], f"layer {l}"
