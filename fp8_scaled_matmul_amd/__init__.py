@@ -31,7 +31,7 @@ FROM_AMAX, GIVEN, FROM_AMAX_POW2 = 0, 1, 2
 EXPORTED = [
     "fp8_abi_version", "fp8_status_string", "fp8_last_error",
     "fp8_amax_workspace_size", "fp8_amax",
-    "fp8_quantize_workspace_size", "fp8_quantize",
+    "fp8_quantize_workspace_size", "fp8_quantize", "fp8_quantize_noalloc",
     "fp8_quantize_delayed_workspace_size", "fp8_quantize_delayed",
     "fp8_scaled_mm_workspace_size", "fp8_scaled_mm",
     "fp8_requant_workspace_size", "fp8_requant_weights",
@@ -79,6 +79,9 @@ def lib():
         L.fp8_quantize.restype = i32
         L.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, vp,
                                    vp, i64, vp, i64, vp, vp, sz, vp]
+        L.fp8_quantize_noalloc.restype = i32
+        L.fp8_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, vp,
+                                           vp, i64, vp, i64, vp, vp]
         L.fp8_quantize_delayed_workspace_size.restype = sz
         L.fp8_quantize_delayed_workspace_size.argtypes = [i64, i64]
         L.fp8_quantize_delayed.restype = i32
@@ -125,6 +128,12 @@ def fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, 
                  workspace, workspace_bytes, stream) -> int:
     return lib().fp8_quantize(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
                               workspace, workspace_bytes, stream)
+
+
+def fp8_quantize_noalloc(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
+                         stream) -> int:
+    return lib().fp8_quantize_noalloc(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t, ctr,
+                                      stream)
 
 
 def fp8_quantize_delayed(x, dtype, rows, cols, ld, fmt, history, pos, history_len, scale, q, ldq, q_t, ldq_t,

@@ -200,6 +200,47 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
     return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize launch");
 }
 
+fp8_status fp8_quantize_noalloc(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                                fp8_format fmt, fp8_granularity gran, fp8_scale_mode mode, float* scale,
+                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t, fp8_counters* ctr,
+                                hipStream_t stream)
+{
+    // the scratch must hold every partial the call's workspace would: the
+    // per-tensor amax pass writes at most kAmaxPartials keys for any size
+    const size_t need = fp8_quantize_workspace_size(rows, cols, gran, mode);
+    if (need > kNoAllocScratchWords * sizeof(uint32_t))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "call needs more scratch than fp8_quantize_noalloc holds (8 KiB)");
+    // the library's scratch stands in for the workspace argument: checked as
+    // present and large enough (its address is resolved after the checks)
+    void* const scratch_stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+    fp8_status s = check_quantize_args(x, dtype, rows, cols, ld, fmt, gran, mode, scale, q, ldq, q_t, ldq_t,
+                                       scratch_stand_in, kNoAllocScratchWords * sizeof(uint32_t));
+    if (s != FP8_OK) return s;
+    if ((s = check_device()) != FP8_OK) return s;
+    uint32_t* scratch = nullptr;
+    hipError_t e = noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "fp8_quantize_noalloc scratch address");
+    QuantArgs a;
+    a.x = x;
+    a.dtype = dtype;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld;
+    a.fmt = fmt;
+    a.gran = gran;
+    a.mode = amax_mode(mode) ? FP8_SCALE_FROM_AMAX : mode;
+    a.pow2 = mode == FP8_SCALE_FROM_AMAX_POW2;
+    a.scale = scale;
+    a.q = q;
+    a.ldq = ldq;
+    a.qt = q_t;
+    a.ldqt = ldq_t;
+    a.ctr = ctr;
+    a.partials = scratch;
+    e = launch_quantize(a, stream);
+    return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize_noalloc launch");
+}
+
 size_t fp8_quantize_delayed_workspace_size(int64_t rows, int64_t cols)
 {
     (void)rows;

@@ -14,6 +14,14 @@ namespace fp8mi {
 constexpr int kAmaxPartials = 2048;
 constexpr size_t kAmaxWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
 
+// Library-owned scratch of fp8_quantize_noalloc: room for the amax partials
+// of one call (the largest count any tensor size produces), per device.
+constexpr int kNoAllocScratchWords = kAmaxPartials;
+constexpr int kMaxScratchDevices = 64;
+// The calling thread's current device's scratch address (resolved once per
+// device with hipGetSymbolAddress).
+hipError_t noalloc_scratch(uint32_t** out);
+
 // Quantizer launch description (all pointers device pointers).
 struct QuantArgs {
     const void* x;

@@ -12,6 +12,7 @@
 // is two passes (amax partials, then cast) with the scale kept on the device;
 // fine-grained scaling is one fused pass per tile or block.
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "fastdiv.h"
@@ -1160,6 +1161,38 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ library-owned scratch
+// The per-tensor amax partials of fp8_quantize_noalloc live in this array
+// rather than in a caller's workspace: one copy per device, loaded with the
+// code object and held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it asks the runtime for the device address once per device and
+// passes that.
+static __device__ __align__(256) uint32_t scratch[kNoAllocScratchWords];
+
+namespace {
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(uint32_t** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)

@@ -148,6 +148,26 @@ fp8_status fp8_quantize(const void* x, fp8_dtype dtype, int64_t rows, int64_t co
                         fp8_counters* ctr,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* fp8_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what fp8_quantize
+ * does with the same arguments.  The per-tensor amax partials it needs
+ * (TENSOR with FROM_AMAX or FROM_AMAX_POW2) go to a scratch array the
+ * library holds in device memory: 8 KiB per device, loaded with the library
+ * and kept until the process ends; its address is resolved once per device
+ * on the first call made with that device current.  No size needs more than
+ * those 8 KiB (a call that would gets FP8_ERR_UNSUPPORTED_SHAPE).  Every call
+ * on a device shares that device's scratch, and nothing in it has to start
+ * at zero (each call writes the partials it reads); calls that overlap in
+ * time on one device -- on different streams, or from different threads
+ * without ordering -- race on it and may produce wrong scales.  Calls on
+ * one stream are ordered and safe. */
+fp8_status fp8_quantize_noalloc(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                                fp8_format fmt, fp8_granularity gran, fp8_scale_mode mode,
+                                float* scale,
+                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                fp8_counters* ctr, hipStream_t stream);
+
 /* ------------------------------------------------------------------ delayed scaling
  * Per-tensor quantize with delayed scaling and an amax history (the
  * guardrails explainer, "Real products": Transformer Engine's delayed
