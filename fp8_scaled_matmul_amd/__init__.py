@@ -34,6 +34,7 @@ EXPORTED = [
     "fp8_quantize_workspace_size", "fp8_quantize", "fp8_quantize_noalloc",
     "fp8_quantize_delayed_workspace_size", "fp8_quantize_delayed",
     "fp8_scaled_mm_workspace_size", "fp8_scaled_mm",
+    "fp8_quantize_scaled_mm_workspace_size", "fp8_quantize_scaled_mm",
     "fp8_requant_workspace_size", "fp8_requant_weights",
     "fp8_counters_reset",
 ]
@@ -92,6 +93,11 @@ def lib():
         L.fp8_scaled_mm.restype = i32
         L.fp8_scaled_mm.argtypes = [vp, i32, i64, vp, i32, vp, i32, i64, vp, i32,
                                     i64, i64, i64, vp, i64, vp, sz, vp, vp]
+        L.fp8_quantize_scaled_mm_workspace_size.restype = sz
+        L.fp8_quantize_scaled_mm_workspace_size.argtypes = [i64, i64, i64]
+        L.fp8_quantize_scaled_mm.restype = i32
+        L.fp8_quantize_scaled_mm.argtypes = [vp, i64, i32, vp, vp, i64, vp, i64, vp, i32, i64, vp,
+                                             i64, i64, i64, vp, i64, vp, vp, sz, vp]
         L.fp8_requant_workspace_size.restype = sz
         L.fp8_requant_workspace_size.argtypes = [ctypes.POINTER(WeightCacheDesc), ctypes.c_int32]
         L.fp8_requant_weights.restype = i32
@@ -148,6 +154,12 @@ def fp8_scaled_mm(a, fa, lda, scale_a, ga, b, fb, ldb, scale_b, gb, m, n, k, c, 
                                workspace, workspace_bytes, ctr, stream)
 
 
+def fp8_quantize_scaled_mm(x, ldx, fa, scale_a, xq, ldxq, xq_t, ldxq_t, b, fb, ldb, scale_b, m, n, k, c, ldc,
+                           ctr, workspace, workspace_bytes, stream) -> int:
+    return lib().fp8_quantize_scaled_mm(x, ldx, fa, scale_a, xq, ldxq, xq_t, ldxq_t, b, fb, ldb, scale_b, m, n, k,
+                                        c, ldc, ctr, workspace, workspace_bytes, stream)
+
+
 def fp8_requant_weights(descs, masters, dtypes, workspace, workspace_bytes, stream) -> int:
     n = len(descs)
     arr = (WeightCacheDesc * n)(*descs)
@@ -184,6 +196,11 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _ld(t):
+    """Leading dimension of a 2-D tensor (an empty tensor's stride may be 0)."""
+    return t.stride(0) if t.shape[0] > 0 else max(t.shape[1], 1)
+
+
 # Host-side checks of every tensor handed to the C ABI.  The library sees raw
 # device pointers and cannot tell an undersized, mistyped or host-resident
 # buffer from a good one, so the binding checks dtype, shape, strides and
@@ -199,7 +216,7 @@ def _check_tensor(t, name, dtypes, shape=None, contiguous=False, unit_col_stride
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if unit_col_stride and (t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1)):
+    if unit_col_stride and (t.dim() != 2 or (t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1)):
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
 
 
@@ -304,9 +321,9 @@ def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scal
         qt = out_t if out_t is not None else torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
     wsb = lib().fp8_quantize_workspace_size(rows, cols, gran, mode)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
-    check(fp8_quantize(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), fmt, gran, mode,
-                       scale.data_ptr(), q.data_ptr(), q.stride(0),
-                       _ptr(qt), qt.stride(0) if qt is not None else 0,
+    check(fp8_quantize(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), fmt, gran, mode,
+                       scale.data_ptr(), q.data_ptr(), _ld(q),
+                       _ptr(qt), _ld(qt) if qt is not None else 0,
                        counters.ptr() if counters else None, ws.data_ptr(), wsb, _stream()))
     return q, qt, scale
 
@@ -385,12 +402,53 @@ def scaled_mm(a, fa: int, scale_a, ga: int, b, fb: int, scale_b, gb: int,
     wsb = lib().fp8_scaled_mm_workspace_size(m, n, k, ga, gb)
     if workspace is None and wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
-    check(fp8_scaled_mm(a.data_ptr(), fa, a.stride(0), scale_a.data_ptr(), ga,
-                        b.data_ptr(), fb, b.stride(0), scale_b.data_ptr(), gb,
-                        m, n, k, c.data_ptr(), c.stride(0),
+    check(fp8_scaled_mm(a.data_ptr(), fa, _ld(a), scale_a.data_ptr(), ga,
+                        b.data_ptr(), fb, _ld(b), scale_b.data_ptr(), gb,
+                        m, n, k, c.data_ptr(), _ld(c),
                         _ptr(workspace), workspace.numel() if workspace is not None else 0,
                         counters.ptr() if counters else None, _stream()))
     return c
+
+
+def quantize_scaled_mm(x, fa: int, b, fb: int, scale_b, out=None, want_q: bool = False, want_t: bool = False,
+                       counters: Counters | None = None, scale_a=None, out_q=None, out_t=None, workspace=None):
+    """The forward projection with its bf16 activation quantized on the way
+    in: y = bf16(s_a s_b (Q(x) B^T)) with s_a the per-tensor amax scale of x.
+    x bf16 [m, 768], b uint8 [n, 768].  Returns (y, scale_a, xq or None,
+    xq_t or None); the codes equal those of quantize(x, fa, TENSOR)."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.bfloat16,), unit_col_stride=True)
+    _check_tensor(b, "b", (torch.uint8,), unit_col_stride=True)
+    m, k = x.shape
+    n, k2 = b.shape
+    if k != k2:
+        raise ValueError("x and b disagree on k")
+    _check_scale(scale_b, "scale_b", TENSOR, n, k)
+    if scale_a is not None:
+        _check_scale(scale_a, "scale_a", TENSOR, m, k)
+    if out is not None:
+        _check_tensor(out, "out", (torch.bfloat16,), (m, n), unit_col_stride=True)
+    if out_q is not None:
+        _check_tensor(out_q, "out_q", (torch.uint8,), (m, k), unit_col_stride=True)
+    if out_t is not None:
+        _check_tensor(out_t, "out_t", (torch.uint8,), (k, m), unit_col_stride=True)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", (torch.uint8,), contiguous=True)
+    _check_devices(x, b, scale_b, scale_a, out, out_q, out_t, workspace, counters.buf if counters else None)
+    c = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    sa = scale_a if scale_a is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    xq = out_q if out_q is not None else (torch.empty((m, k), dtype=torch.uint8, device=x.device) if want_q else None)
+    xqt = out_t if out_t is not None else (torch.empty((k, m), dtype=torch.uint8, device=x.device) if want_t else None)
+    wsb = lib().fp8_quantize_scaled_mm_workspace_size(m, n, k)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    check(fp8_quantize_scaled_mm(x.data_ptr(), _ld(x), fa, sa.data_ptr(),
+                                 _ptr(xq), _ld(xq) if xq is not None else 0,
+                                 _ptr(xqt), _ld(xqt) if xqt is not None else 0,
+                                 b.data_ptr(), fb, _ld(b), scale_b.data_ptr(), m, n, k,
+                                 c.data_ptr(), _ld(c), counters.ptr() if counters else None,
+                                 workspace.data_ptr(), workspace.numel(), _stream()))
+    return c, sa, xq, xqt
 
 
 class WeightCache:

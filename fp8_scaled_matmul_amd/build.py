@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8mi.so")
 
-SOURCES = ["quantize.hip", "gemm.hip", "gemm_persistent.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "gemm_persistent.hip", "gemm_astat.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -30,7 +30,10 @@ FLAGS = [
 
 # Per-file extras.  The block-scaled GEMM promotes each MFMA result on the
 # VALU: MFMA results written straight to VGPRs save a copy out of AGPRs.
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # the A-stationary kernel's 72-step unit loop must unroll fully (its
+         # register rings are indexed by the step)
+         "gemm_astat.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
 
 
 def _compile(src: str) -> str:

@@ -348,6 +348,92 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda, const flo
     return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_scaled_mm launch");
 }
 
+size_t fp8_quantize_scaled_mm_workspace_size(int64_t m, int64_t n, int64_t k)
+{
+    (void)m;
+    (void)n;
+    (void)k;
+    return kAmaxWorkspaceBytes;
+}
+
+fp8_status fp8_quantize_scaled_mm(const void* x, int64_t ldx, fp8_format fa, float* scale_a, uint8_t* xq, int64_t ldxq,
+                                  uint8_t* xq_t, int64_t ldxq_t, const uint8_t* b, fp8_format fb, int64_t ldb,
+                                  const float* scale_b, int64_t m, int64_t n, int64_t k, void* c_bf16, int64_t ldc,
+                                  fp8_counters* ctr, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8_ERR_INVALID_ARG, "unknown FP8 format");
+    fp8_status s;
+    if ((s = check_2d(x, m, k, ldx, "x")) != FP8_OK) return s;
+    if ((s = check_2d(b, n, k, ldb, "b")) != FP8_OK) return s;
+    if ((s = check_2d(c_bf16, m, n, ldc, "c")) != FP8_OK) return s;
+    if (xq && (s = check_2d(xq, m, k, ldxq, "xq")) != FP8_OK) return s;
+    if (xq_t && (s = check_2d(xq_t, k, m, ldxq_t, "xq_t")) != FP8_OK) return s;
+    if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "scale: null pointer");
+    if (!workspace || workspace_bytes < kAmaxWorkspaceBytes)
+        return fail(FP8_ERR_INVALID_ARG, "workspace smaller than fp8_quantize_scaled_mm_workspace_size()");
+    if (k != kAstatK) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "fp8_quantize_scaled_mm takes k == 768");
+    const auto mis = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+    if (mis(x, 16) || ldx % 8 != 0) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "x: rows must start on 16-byte boundaries");
+    if (mis(b, 16) || ldb % 16 != 0) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "b: rows must start on 16-byte boundaries");
+    if (xq && (mis(xq, 16) || ldxq % 16 != 0))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "xq: rows must start on 16-byte boundaries");
+    if (n > 0 && (n % 4 != 0 || ldc % 4 != 0 || mis(c_bf16, 8)))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "n and ldc must be multiples of 4 and c 8-byte aligned");
+    if (ldx >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 22) || ldc >= ((int64_t)1 << 21) || m >= ((int64_t)1 << 31) ||
+        n >= ((int64_t)1 << 31))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "ldx, ldb below 2^22, ldc below 2^21, m and n below 2^31");
+    if ((s = check_device()) != FP8_OK) return s;
+    hipError_t e;
+    if (m == 0) {
+        // an empty activation: scale 1, nothing else to write
+        QuantArgs a;
+        a.x = x;
+        a.dtype = FP8_IN_BF16;
+        a.rows = 0;
+        a.cols = k;
+        a.ld = ldx;
+        a.fmt = fa;
+        a.gran = FP8_TENSOR;
+        a.mode = FP8_SCALE_FROM_AMAX;
+        a.scale = scale_a;
+        a.q = xq;
+        a.ldq = ldxq;
+        a.qt = nullptr;
+        a.ldqt = 0;
+        a.ctr = ctr;
+        a.partials = static_cast<uint32_t*>(workspace);
+        e = launch_quantize(a, stream);
+        return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize_scaled_mm launch");
+    }
+    int np = 0;
+    e = launch_amax_partials(x, FP8_IN_BF16, m, k, ldx, static_cast<uint32_t*>(workspace), &np, stream);
+    if (e != hipSuccess) return hip_fail(e, "fp8_quantize_scaled_mm amax launch");
+    AstatArgs g;
+    g.a = x;
+    g.lda = ldx;
+    g.bf16_a = true;
+    g.fa = fa;
+    g.b = b;
+    g.ldb = ldb;
+    g.fb = fb;
+    g.sa = nullptr;
+    g.sa_out = scale_a;
+    g.sb = scale_b;
+    g.partials = static_cast<const uint32_t*>(workspace);
+    g.np = np;
+    g.xq = xq;
+    g.ldxq = ldxq;
+    g.xqt = xq_t;
+    g.ldxqt = ldxq_t;
+    g.m = m;
+    g.n = n;
+    g.c = c_bf16;
+    g.ldc = ldc;
+    g.ctr = ctr;
+    e = launch_gemm_astat(g, gemm_num_cus(), stream);
+    return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_quantize_scaled_mm launch");
+}
+
 size_t fp8_requant_workspace_size(const fp8_weight_cache* caches, int32_t count)
 {
     if (!caches || count <= 0) return 0;

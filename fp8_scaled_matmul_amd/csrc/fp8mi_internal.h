@@ -91,6 +91,39 @@ struct GemmArgs {
     fp8_counters* ctr;
 };
 
+// A-stationary per-tensor GEMM (gemm_astat.hip): K is one model width, the
+// whole [192, K] panel of A codes stays in LDS.  A is FP8 codes, or bf16
+// quantized on the way in with the amax scale of `partials`.
+constexpr int kAstatK = 768;
+struct AstatArgs {
+    const void* a;
+    int64_t lda;        // elements of A's dtype
+    bool bf16_a;
+    int fa;
+    const uint8_t* b;
+    int64_t ldb;
+    int fb;
+    const float* sa;    // FP8 A: its scale
+    float* sa_out;      // bf16 A: the scale written
+    const float* sb;
+    const uint32_t* partials;   // bf16 A: amax partial keys
+    int np;
+    uint8_t* xq;        // bf16 A, optional outputs: codes [m, k] and transposed [k, m]
+    int64_t ldxq;
+    uint8_t* xqt;
+    int64_t ldxqt;
+    int64_t m, n;
+    void* c;
+    int64_t ldc;
+    fp8_counters* ctr;
+};
+bool astat_supported(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, int64_t ldc, const void* c);
+hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream);
+// The first pass of per-tensor quantization: amax partial keys of x; *np
+// receives their count (at most kAmaxPartials).
+hipError_t launch_amax_partials(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t* partials, int* np, hipStream_t stream);
+
 int gemm_choose_splits(int64_t m, int64_t n, int64_t k);
 int gemm_num_cus();
 hipError_t launch_gemm_persistent(const GemmArgs& g, int num_cus, hipStream_t stream);

@@ -902,6 +902,34 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream)
     // kernel.  Measured in the step: 3072x768x65536 (split) 14% and
     // 65536x768x3072 3% faster on the 8-wave kernel, 65536x3072x768 (6 blocks
     // per tile) 2% slower.
+    // Per-tensor GEMMs whose K is one model width (768) and that do not split
+    // K: the A-stationary kernel (the whole [192, 768] A panel in LDS, only B
+    // streams).
+    if (!g.block_scaled && !p.ws && astat_supported(g.m, g.n, g.k, g.lda, g.ldb, g.ldc, g.c)) {
+        AstatArgs a;
+        a.a = g.a;
+        a.lda = g.lda;
+        a.bf16_a = false;
+        a.fa = g.fa;
+        a.b = g.b;
+        a.ldb = g.ldb;
+        a.fb = g.fb;
+        a.sa = g.sa;
+        a.sa_out = nullptr;
+        a.sb = g.sb;
+        a.partials = nullptr;
+        a.np = 0;
+        a.xq = nullptr;
+        a.ldxq = 0;
+        a.xqt = nullptr;
+        a.ldxqt = 0;
+        a.m = g.m;
+        a.n = g.n;
+        a.c = g.c;
+        a.ldc = g.ldc;
+        a.ctr = g.ctr;
+        return launch_gemm_astat(a, gemm_num_cus(), stream);
+    }
     const bool tensor_via_block = !g.block_scaled && g.k % BK == 0 && (p.ws || g.k >= 16 * BK);
     if (!g.block_scaled && !tensor_via_block) {
         e = launch_gemm_persistent(g, gemm_num_cus(), stream);

@@ -1321,6 +1321,23 @@ hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos
     return hipGetLastError();
 }
 
+hipError_t launch_amax_partials(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t* partials, int* np, hipStream_t stream)
+{
+    const int eb = dtype == FP8_IN_BF16 ? 2 : 4;
+    int64_t r = rows, c = cols, l = ld;
+    flatten(r, c, l);
+    const int vec = aligned16(x) && (r == 1 || (l * eb) % 16 == 0);
+    dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+    if (rows == 0 || cols == 0) { r = 0; g = dim3(1, 1, 1); }
+    if (dtype == FP8_IN_BF16)
+        hipLaunchKernelGGL(k_amax_partials<0>, g, dim3(kThreads), 0, stream, x, r, c, l, vec, partials);
+    else
+        hipLaunchKernelGGL(k_amax_partials<1>, g, dim3(kThreads), 0, stream, x, r, c, l, vec, partials);
+    *np = (int)(g.x * g.y);
+    return hipGetLastError();
+}
+
 hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* out,
                               uint32_t* partials, hipStream_t stream)
 {

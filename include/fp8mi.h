@@ -237,6 +237,40 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, int64_t lda,
                          void* workspace, size_t workspace_bytes,
                          fp8_counters* ctr, hipStream_t stream);
 
+/* ------------------------------------------------------------------ quantize + GEMM
+ * The forward projection with its activation quantized on the way into the
+ * GEMM: x is bf16 [m, k]; one call computes
+ *     s_a = the FROM_AMAX per-tensor scale of x (written to scale_a),
+ *     q   = the codes of x exactly as fp8_quantize(x, fa, TENSOR, FROM_AMAX)
+ *           gives them (written to xq and/or its transpose xq_t when those
+ *           are non-NULL; counters added to ctr),
+ *     y   = bf16(s_a s_b sum_k q[m,k] B[n,k]) into c, as fp8_scaled_mm
+ *           (TENSOR, TENSOR) on those codes would.
+ * x is read twice (an amax pass, then the GEMM's operand load, which casts
+ * each 192 x 768 block of rows into LDS once) and the codes need not go
+ * through HBM for the forward product ("FP8 stability guardrails", section
+ * "Why FP8 is tempting and why it is fragile": FP8 halves the activation's
+ * memory traffic; "#84 FP8 Precision", code excerpt: the scaled product).
+ *   x     bf16 [m, k], ldx % 8 == 0, 16-byte aligned.
+ *   xq    optional [m, k] codes, ldxq % 16 == 0, 16-byte aligned.
+ *   xq_t  optional [k, m] codes (the dW operand of the backward pass);
+ *         4-byte stores when xq_t and ldxq_t are 4-byte aligned, byte stores
+ *         otherwise (pad ldxq_t when m is a multiple of 64 KiB, as for
+ *         fp8_quantize).
+ *   b     [n, k] codes, ldb % 16 == 0, 16-byte aligned; scale_b per tensor.
+ *   c     bf16 [m, n]; n and ldc multiples of 4, 8-byte aligned.
+ * Shapes: k == 768 (one panel of A codes fills the LDS), ldx and ldb below
+ * 2^22, ldc below 2^21; other shapes FP8_ERR_UNSUPPORTED_SHAPE (use
+ * fp8_quantize + fp8_scaled_mm).  m == 0 writes scale 1 only.
+ * workspace: fp8_quantize_scaled_mm_workspace_size() bytes (amax partials). */
+size_t     fp8_quantize_scaled_mm_workspace_size(int64_t m, int64_t n, int64_t k);
+fp8_status fp8_quantize_scaled_mm(const void* x, int64_t ldx, fp8_format fa, float* scale_a,
+                                  uint8_t* xq, int64_t ldxq, uint8_t* xq_t, int64_t ldxq_t,
+                                  const uint8_t* b, fp8_format fb, int64_t ldb, const float* scale_b,
+                                  int64_t m, int64_t n, int64_t k,
+                                  void* c_bf16, int64_t ldc, fp8_counters* ctr,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ weight cache
  * The FP8 compute copy of master weights, rebuilt from the bf16 master after
  * every optimizer step and kept for the next forward pass (#84 lab card,
