@@ -753,6 +753,83 @@ __global__ void __launch_bounds__(kThreads)
     flush_counters_block(ctr, sat, und, nan);
 }
 
+// ------------------------------------------------------------------ 128x128 blocks, bf16, no transposed copy
+// One whole 128 x 128 block of a 16-byte aligned bf16 tensor per workgroup
+// of 512 threads; thread t loads the 8 columns 8 (t % 16) of rows t / 16 +
+// 32 j (j = 0..3, four 16-byte loads issued together), the block's amax is
+// a packed max of |x| patterns (exact, flag-carrying merge only for a block
+// holding Inf or NaN), then each thread casts and stores its 32 codes.  Few
+// registers per thread, so every block of a weight-sized tensor is resident
+// at once (the 256-thread tile kernel, at about 195 registers, ran such a
+// tensor in two latency-bound rounds).  SCALE_MODE 1: the scale of each block
+// from its own amax (pow2: the power-of-two rule).
+constexpr int kBlkThreads = 512;
+
+template <int FMT>
+__global__ void __launch_bounds__(kBlkThreads) k_block128_bf16(const uint16_t* x, int64_t ld, int64_t blocks_c,
+                                                               float* scale, int64_t scale_ld, uint8_t* q,
+                                                               int64_t ldq, fp8_counters* ctr, int pow2)
+{
+    __shared__ uint32_t sh[kBlkThreads / 64];
+    const int t = threadIdx.x;
+    const int64_t br = blockIdx.x / blocks_c, bc = blockIdx.x - br * blocks_c;
+    const int64_t r0 = br * kTile + (t >> 4), c0 = bc * kTile + 8 * (t & 15);
+    uint4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = ld_stream(x + (r0 + 32 * j) * ld + c0);
+    us2 pk = us2{0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pk = pkmax8(pk, w[j]);
+    uint32_t key = wave_max(pk_raw(pk));
+    if ((t & 63) == 0) sh[t >> 6] = key;
+    __syncthreads();
+    key = sh[0];
+#pragma unroll
+    for (int i = 1; i < kBlkThreads / 64; ++i) key = max(key, sh[i]);
+    if (key >= kRawNonFinite) {
+        // an Inf or NaN in the block: the exact merge (finite amax + flag)
+        __syncthreads();
+        uint32_t e = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t ws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
+                e = key_merge(e, absbits_bf16(ws[h] >> 16));
+            }
+        }
+        e = wave_key_merge(e);
+        if ((t & 63) == 0) sh[t >> 6] = e;
+        __syncthreads();
+        key = sh[0];
+        for (int i = 1; i < kBlkThreads / 64; ++i) key = key_merge(key, sh[i]);
+    }
+    const float s = scale_rule<FMT>(key_amax(key), pow2);
+    if (t == 0) scale[br * scale_ld + bc] = s;
+    const bool fast = !key_special(key) && s >= kCorrectedQuotMinScale;
+    uint32_t sat = 0, und = 0, nan = 0;
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t ws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+        uint2 o;
+        if (fast) {
+            o = cast8_bf16_fast<FMT>(ws, s, r, und);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[2 * h] = bf16_lo(ws[h]);
+                v[2 * h + 1] = bf16_hi(ws[h]);
+            }
+            o = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+        }
+        *reinterpret_cast<uint2*>(q + (r0 + 32 * j) * ldq + c0) = o;
+    }
+    flush_counters_block(ctr, sat, und, nan);
+}
+
 // ------------------------------------------------------------------ 1x128 row tiles, bf16 fast path
 // Full tiles of a 16-byte aligned bf16 tensor, scale from each tile's amax.
 // 16 lanes per tile and 4 tiles per group and iteration, all loads first.
@@ -1078,7 +1155,16 @@ hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int 
     const int64_t nt = cdiv(rows, kTile) * cdiv(cols, kTile);
     const int64_t nfull = (rows / kTile) * (cols / kTile);
     int only_partial = 0;
-    if (DT == 0 && vec && nfull > 0) {
+    if (DT == 0 && vec && nfull > 0 && nfull <= INT32_MAX && SCALE_MODE == 1 && !a.qt) {
+        // per-block amax and no transposed copy: one block per 512 threads
+        const int64_t blocks_c = cols / kTile;
+        hipLaunchKernelGGL((k_block128_bf16<FMT>), dim3((unsigned)nfull), dim3(kBlkThreads), 0, stream,
+                           static_cast<const uint16_t*>(a.x), a.ld, blocks_c, a.scale, cdiv(cols, kTile), a.q, a.ldq,
+                           a.ctr, a.pow2);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || nfull == nt) return e;
+        only_partial = 1;
+    } else if (DT == 0 && vec && nfull > 0) {
         // a workgroup is 4 waves, one per SIMD: per-tensor mode fills each CU once
         const int per_cu = SCALE_MODE == 0 ? kTileWavesPerSimd0 : 4;
         const int grid = (int)std::min<int64_t>(nfull, (int64_t)num_cus() * per_cu);
@@ -1217,6 +1303,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)
 hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream)
 {
     hipError_t e;
+    // one cache: the single-tensor path (its bf16 tile kernel is faster than
+    // the batch's general tile code; the launch count is the same)
+    if (count == 1) return launch_quantize(caches[0], stream);
     for (int g0 = 0; g0 < count; g0 += kRequantMaxCaches) {
         RequantBatch bt{};
         int wg = 0;

@@ -66,6 +66,7 @@ def test_block_scaled_workload_full_size():
     b = synth.channel_scaled_bf16(4, 1, 4, synth.BLOCK_SCALED["b"])
     _cmp_pow2(a, fm.E4M3, fm.ROW_1x128)
     _cmp_pow2(b, fm.E4M3, fm.BLOCK_128x128, want_t=True)
+    _cmp_pow2(b, fm.E4M3, fm.BLOCK_128x128)
 
 
 # ------------------------------------------------------------------ GEMM with E8M0 scales in the MFMA

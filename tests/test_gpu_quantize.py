@@ -79,6 +79,44 @@ def test_row_tiles_thousands_of_scales(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_block_tiles_thousands_of_scales(fmt):
+    """Each 128x128 block has its own amax over the whole bf16 range (full
+    blocks plus a ragged edge, with and without the transposed copy), then
+    Inf and NaN in a few blocks: scales, codes and counters exact."""
+    g = np.random.default_rng(12)
+    rows, cols = 1024 + 40, 1536 + 72
+    x = g.integers(0, 65536, size=(rows, cols)).astype(np.uint16)
+    br, bc = np.arange(rows)[:, None] // 128, np.arange(cols)[None, :] // 128
+    cap = g.integers(1, 0xFF, size=(rows // 128 + 1, cols // 128 + 1)).astype(np.uint16)[br, bc]
+    x = (x & 0x807F) | (np.minimum(cap, (x >> 7) & 0xFF) << 7).astype(np.uint16)
+    _cmp(x, fmt, fm.BLOCK_128x128)
+    _cmp(x, fmt, fm.BLOCK_128x128, want_t=True)
+    x2 = x.copy()
+    x2[g.integers(0, rows, 30), g.integers(0, cols, 30)] = 0x7F80
+    x2[g.integers(0, rows, 30), g.integers(0, cols, 30)] = 0xFFC1
+    x2[5, 7] = 0xFF80
+    _cmp(x2, fmt, fm.BLOCK_128x128)
+    _cmp(x2, fmt, fm.BLOCK_128x128, want_t=True)
+
+
+def test_block_strided_full_tiles():
+    """Full 128x128 blocks of a strided input into a strided output: the
+    padding of the output is never written."""
+    x_full = synth.with_outliers_bf16(13, (300, 600), frac=0.01)
+    x = dev_bf16(x_full)[:, 8:520]            # ld 600, cols 512
+    xo = np.ascontiguousarray(x_full[:, 8:520])
+    out = torch.full((300, 544), 0xAA, dtype=torch.uint8, device="cuda")
+    ctr = fm.Counters()
+    _, _, s = fm.quantize(x, fm.E5M2, fm.BLOCK_128x128, fm.FROM_AMAX, out=out[:, :512], counters=ctr)
+    oq, _, os_, oc = oracle.quantize(xo, fm.E5M2, fm.BLOCK_128x128)
+    got = host(out)
+    assert np.array_equal(got[:, :512], oq)
+    assert np.all(got[:, 512:] == 0xAA), "wrote past cols"
+    assert np.array_equal(host(s).reshape(os_.shape), os_)
+    assert same_counters(ctr.read(), oc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", [(128, 128), (256, 384), (200, 300), (1, 5), (129, 127), (7, 1000)])
 def test_block_128_and_transpose(fmt, shape):
     x = synth.with_outliers_bf16(2, shape, frac=0.01)
