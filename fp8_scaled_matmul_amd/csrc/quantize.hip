@@ -754,32 +754,43 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ------------------------------------------------------------------ 128x128 blocks, bf16, no transposed copy
-// One whole 128 x 128 block of a 16-byte aligned bf16 tensor per workgroup
-// of 512 threads; thread t loads the 8 columns 8 (t % 16) of rows t / 16 +
-// 32 j (j = 0..3, four 16-byte loads issued together), the block's amax is
-// a packed max of |x| patterns (exact, flag-carrying merge only for a block
-// holding Inf or NaN), then each thread casts and stores its 32 codes.  Few
-// registers per thread, so every block of a weight-sized tensor is resident
-// at once (the 256-thread tile kernel, at about 195 registers, ran such a
-// tensor in two latency-bound rounds).  SCALE_MODE 1: the scale of each block
-// from its own amax (pow2: the power-of-two rule).
+// Whole 128 x 128 blocks of a 16-byte aligned bf16 tensor, 512 threads per
+// workgroup: thread t holds the 8 columns 8 (t % 16) of rows t / 16 + 32 j
+// (j = 0..3, four 16-byte loads).  Workgroup w takes blocks w, w + G, w + 2G
+// ... (G workgroups) and loads the next block before it reduces and casts the
+// current one, so the loads of later blocks overlap the arithmetic and stores
+// of earlier ones (with one block per workgroup every block's loads end
+// together, and the arithmetic and stores then run with the memory idle).
+// The block's amax is a packed max of |x| patterns; a block holding Inf or NaN
+// redoes the exact, flag-carrying merge.  Scale of each block from its own
+// amax (pow2: the power-of-two rule).
 constexpr int kBlkThreads = 512;
+constexpr int kBlkPerCu = 2;       // workgroups per CU (each walks several blocks)
+constexpr int kBlkOnePerWgMax = 4; // blocks per CU up to which each workgroup takes one
+
+struct BlockRegs {
+    uint4 w[4];
+};
+
+__device__ __forceinline__ void block_load(BlockRegs& b, const uint16_t* x, int64_t ld, int64_t blocks_c,
+                                           int64_t id)
+{
+    const int t = threadIdx.x;
+    const int64_t br = id / blocks_c, bc = id - br * blocks_c;
+    const uint16_t* src = x + (br * kTile + (t >> 4)) * ld + bc * kTile + 8 * (t & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.w[j] = ld_stream(src + 32 * j * ld);
+}
 
 template <int FMT>
-__global__ void __launch_bounds__(kBlkThreads) k_block128_bf16(const uint16_t* x, int64_t ld, int64_t blocks_c,
-                                                               float* scale, int64_t scale_ld, uint8_t* q,
-                                                               int64_t ldq, fp8_counters* ctr, int pow2)
+__device__ __forceinline__ void block_cast(const BlockRegs& b, int64_t id, int64_t blocks_c, uint32_t* sh,
+                                           float* scale, int64_t scale_ld, uint8_t* q, int64_t ldq, int pow2,
+                                           uint32_t& sat, uint32_t& und, uint32_t& nan)
 {
-    __shared__ uint32_t sh[kBlkThreads / 64];
     const int t = threadIdx.x;
-    const int64_t br = blockIdx.x / blocks_c, bc = blockIdx.x - br * blocks_c;
-    const int64_t r0 = br * kTile + (t >> 4), c0 = bc * kTile + 8 * (t & 15);
-    uint4 w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = ld_stream(x + (r0 + 32 * j) * ld + c0);
     us2 pk = us2{0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pk = pkmax8(pk, w[j]);
+    for (int j = 0; j < 4; ++j) pk = pkmax8(pk, b.w[j]);
     uint32_t key = wave_max(pk_raw(pk));
     if ((t & 63) == 0) sh[t >> 6] = key;
     __syncthreads();
@@ -792,7 +803,7 @@ __global__ void __launch_bounds__(kBlkThreads) k_block128_bf16(const uint16_t* x
         uint32_t e = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t ws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+            const uint32_t ws[4] = {b.w[j].x, b.w[j].y, b.w[j].z, b.w[j].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
@@ -805,14 +816,15 @@ __global__ void __launch_bounds__(kBlkThreads) k_block128_bf16(const uint16_t* x
         key = sh[0];
         for (int i = 1; i < kBlkThreads / 64; ++i) key = key_merge(key, sh[i]);
     }
+    const int64_t br = id / blocks_c, bc = id - br * blocks_c;
     const float s = scale_rule<FMT>(key_amax(key), pow2);
     if (t == 0) scale[br * scale_ld + bc] = s;
     const bool fast = !key_special(key) && s >= kCorrectedQuotMinScale;
-    uint32_t sat = 0, und = 0, nan = 0;
     const float r = 1.0f / s;
+    uint8_t* dst = q + (br * kTile + (t >> 4)) * ldq + bc * kTile + 8 * (t & 15);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t ws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+        const uint32_t ws[4] = {b.w[j].x, b.w[j].y, b.w[j].z, b.w[j].w};
         uint2 o;
         if (fast) {
             o = cast8_bf16_fast<FMT>(ws, s, r, und);
@@ -825,8 +837,39 @@ __global__ void __launch_bounds__(kBlkThreads) k_block128_bf16(const uint16_t* x
             }
             o = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
         }
-        *reinterpret_cast<uint2*>(q + (r0 + 32 * j) * ldq + c0) = o;
+        *reinterpret_cast<uint2*>(dst + 32 * j * ldq) = o;
     }
+}
+
+// PIPE false: one block per workgroup (a tensor of at most 4 blocks per CU:
+// at about 60 registers all of them are resident at once, which beats the
+// pipelined walk there); PIPE true: the walk above, two workgroups per CU.
+template <int FMT, bool PIPE>
+__global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(PIPE ? 4 : 8))) k_block128_bf16(const uint16_t* x, int64_t ld, int64_t blocks_c,
+                                                               int64_t nblocks, float* scale, int64_t scale_ld,
+                                                               uint8_t* q, int64_t ldq, fp8_counters* ctr, int pow2)
+{
+    // two slots: the block after next writes its wave maxima only after every
+    // thread has passed the current block's barrier
+    __shared__ uint32_t sh[2][kBlkThreads / 64];
+    uint32_t sat = 0, und = 0, nan = 0;
+    const int64_t G = gridDim.x;
+    int64_t id = blockIdx.x;
+    BlockRegs b0, b1;
+    block_load(b0, x, ld, blocks_c, id);
+    // unrolled by two so the register sets alternate statically
+    while (PIPE) {
+        const int64_t id1 = id + G;
+        if (id1 < nblocks) block_load(b1, x, ld, blocks_c, id1);
+        block_cast<FMT>(b0, id, blocks_c, sh[0], scale, scale_ld, q, ldq, pow2, sat, und, nan);
+        if (id1 >= nblocks) break;
+        const int64_t id2 = id1 + G;
+        if (id2 < nblocks) block_load(b0, x, ld, blocks_c, id2);
+        block_cast<FMT>(b1, id1, blocks_c, sh[1], scale, scale_ld, q, ldq, pow2, sat, und, nan);
+        if (id2 >= nblocks) break;
+        id = id2;
+    }
+    if (!PIPE) block_cast<FMT>(b0, id, blocks_c, sh[0], scale, scale_ld, q, ldq, pow2, sat, und, nan);
     flush_counters_block(ctr, sat, und, nan);
 }
 
@@ -1155,12 +1198,17 @@ hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int 
     const int64_t nt = cdiv(rows, kTile) * cdiv(cols, kTile);
     const int64_t nfull = (rows / kTile) * (cols / kTile);
     int only_partial = 0;
-    if (DT == 0 && vec && nfull > 0 && nfull <= INT32_MAX && SCALE_MODE == 1 && !a.qt) {
+    if (DT == 0 && vec && nfull > 0 && SCALE_MODE == 1 && !a.qt) {
         // per-block amax and no transposed copy: one block per 512 threads
         const int64_t blocks_c = cols / kTile;
-        hipLaunchKernelGGL((k_block128_bf16<FMT>), dim3((unsigned)nfull), dim3(kBlkThreads), 0, stream,
-                           static_cast<const uint16_t*>(a.x), a.ld, blocks_c, a.scale, cdiv(cols, kTile), a.q, a.ldq,
-                           a.ctr, a.pow2);
+        const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+        if (nfull <= (int64_t)num_cus() * kBlkOnePerWgMax)
+            hipLaunchKernelGGL((k_block128_bf16<FMT, false>), dim3((unsigned)nfull), dim3(kBlkThreads), 0, stream,
+                               xb, a.ld, blocks_c, nfull, a.scale, cdiv(cols, kTile), a.q, a.ldq, a.ctr, a.pow2);
+        else
+            hipLaunchKernelGGL((k_block128_bf16<FMT, true>), dim3(num_cus() * kBlkPerCu), dim3(kBlkThreads), 0,
+                               stream, xb, a.ld, blocks_c, nfull, a.scale, cdiv(cols, kTile), a.q, a.ldq, a.ctr,
+                               a.pow2);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || nfull == nt) return e;
         only_partial = 1;

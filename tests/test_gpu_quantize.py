@@ -79,12 +79,14 @@ def test_row_tiles_thousands_of_scales(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_block_tiles_thousands_of_scales(fmt):
+@pytest.mark.parametrize("rows,cols", [(1024 + 40, 1536 + 72), (4224 + 40, 4160 + 72)])
+def test_block_tiles_thousands_of_scales(fmt, rows, cols):
     """Each 128x128 block has its own amax over the whole bf16 range (full
     blocks plus a ragged edge, with and without the transposed copy), then
-    Inf and NaN in a few blocks: scales, codes and counters exact."""
+    Inf and NaN in a few blocks: scales, codes and counters exact.  96 full
+    blocks take one workgroup each; 1056 (more than four per CU) are walked
+    by fewer workgroups, each loading its next block ahead."""
     g = np.random.default_rng(12)
-    rows, cols = 1024 + 40, 1536 + 72
     x = g.integers(0, 65536, size=(rows, cols)).astype(np.uint16)
     br, bc = np.arange(rows)[:, None] // 128, np.arange(cols)[None, :] // 128
     cap = g.integers(1, 0xFF, size=(rows // 128 + 1, cols // 128 + 1)).astype(np.uint16)[br, bc]
