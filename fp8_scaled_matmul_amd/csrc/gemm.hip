@@ -19,12 +19,15 @@
 //     power-of-two form uses v_mfma_scale_f32_16x16x128_f8f6f4 and needs no
 //     promotion);
 //   - A and B K blocks (2 x 32 KB) are double buffered in LDS, filled by
-//     buffer_load ... lds DMA: B early in the block two K blocks ahead, A
-//     after the block's last A read; s_a arrives by DMA two K blocks ahead and
-//     the workgroup turns it into s_a s_b per row and N block once, in LDS;
+//     buffer_load ... lds DMA two K blocks ahead: B early in the block, A in
+//     two halves, each as soon as every wave has read the rows it refills,
+//     so the requests are spread over the block; s_a arrives by DMA two K
+//     blocks ahead and the workgroup turns it into s_a s_b per row and N
+//     block once, in LDS;
 //   - operand fragments, the next K block's included, are read from LDS
-//     while the MFMAs run; two barriers per K block: one once every wave
-//     holds the block's B fragments, one after the last read of its A data;
+//     while the MFMAs run; three barriers per K block: once every wave holds
+//     the block's B fragments, after the read of A fragment group 3, and
+//     after the block's last A read;
 //   - B rows are permuted in LDS so that each lane ends up with 4 adjacent
 //     output columns (8-byte bf16 stores).
 #include <hip/hip_bf16.h>
@@ -120,19 +123,39 @@ __device__ inline void dma16_so(uint32_t lds, uint32_t voff, const v4u& rsrc, ui
 }
 #pragma clang diagnostic pop
 
-// DMA geometry of one wave (w = 0..7).  Instruction j (0..3) of an operand
-// fills LDS rows R = 32 w + 8 j + l/8 (1 KB); lane l writes position l%8 of
-// row R, which receives logical chunk swz(R, l%8) of global row g(R).
-// A: g(R) = R.  B: within each 64-row group, g(R) = 4 (R%16) + (R%64)/16, so
-// that lane p of the fragment at LDS rows 16 j' .. 16 j' + 15 of a group
-// carries output column 4 p + j'.  The swizzle depends on R%16, and rows
-// R and R + 16 differ by 16 (A) or 1 (B) global rows: two lane offsets per
-// operand plus a uniform row step cover the 4 instructions.
+// DMA geometry of one wave (w = 0..7).  Each instruction fills 8 LDS rows
+// (1 KB); lane l writes position l%8 of row R, which receives logical chunk
+// swz(R, l%8) of global row g(R).
+// A: instruction j fills rows R = 128 (w/4) + 32 j + 8 (w%4) + l/8, so the 8
+// waves' instruction j together fill rows 32 j .. 32 j + 31 and 128 + 32 j ..
+// 128 + 32 j + 31: the rows of A fragment groups 2 j and 2 j + 1 of both
+// wave rows, which the K loop refills once every wave has read them;
+// g(R) = R.  B: instruction j fills rows R = 32 w + 8 j + l/8; within each
+// 64-row group g(R) = 4 (R%16) + (R%64)/16, so that lane p of the fragment at
+// LDS rows 16 j' .. 16 j' + 15 of a group carries output column 4 p + j'.
+// The swizzle depends on R%16: one lane offset for A (rows 32 apart), two for
+// B (rows R and R + 16 are 1 global row apart), plus a row step.  The row
+// step is added to the lane offset, not to the uniform offset (which holds
+// only the K offset), so that rows past the operand's end fail the
+// descriptor's range check and read as zeros.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// v + u (u uniform) in a fresh register at each use: written as a volatile
+// instruction so that the compiler does not keep a register per row step
+// alive across the K loop.
+__device__ inline uint32_t add_lane_offset(uint32_t v, uint32_t u)
+{
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(u), "v"(v));
+    return r;
+}
+#pragma clang diagnostic pop
+
 struct BlockDma {
     v4u ra, rb, rs;           // A, B and s_a descriptors of this tile
-    uint32_t va[2], vb[2];    // lane offsets for even and odd j
+    uint32_t va, vb[2];       // lane offsets: A instruction 0; B even and odd j
     uint32_t vs;              // lane offset of this wave's 64 s_a rows
-    uint32_t step_a, step_b;  // byte step between instructions j and j + 2
+    uint32_t step_a, step_b;  // byte step between A instructions j and j + 1, B j and j + 2
     uint32_t lds_a, lds_b, lds_s;   // this wave's LDS targets in stage 0 / ring slot 0 (uniform)
     v4u rsb;                  // s_b descriptor
     uint32_t vsb, lds_sb;     // lanes 0, 1: the tile's two N blocks; others out of range
@@ -149,18 +172,21 @@ __device__ inline BlockDma block_dma(const KArgs& p, int m0, int n0, int w, bool
     const int nkb = p.k / BK;
     // per-tensor scales: no scale blocks to fetch (zero-length descriptors)
     d.rs = gemm::make_rsrc(p.sa + (int64_t)m0 * nkb, block_scales ? (uint32_t)(rows_a * nkb * 4) : 0u);
+    {
+        const int R = 128 * (w >> 2) + 8 * (w & 3) + q;
+        d.va = (uint32_t)(R * p.lda + 16 * gemm::swz(R, pos));
+    }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int R = 32 * w + 8 * e + q;
         const int c = gemm::swz(R, pos);
-        d.va[e] = (uint32_t)(R * p.lda + 16 * c);
         const int g = 64 * (w >> 1) + 32 * e + 4 * q + 2 * (w & 1);
         d.vb[e] = (uint32_t)(g * p.ldb + 16 * c);
     }
     d.vs = (uint32_t)((64 * (w & 3) + l) * nkb * 4);
-    d.step_a = (uint32_t)(16 * p.lda);
+    d.step_a = (uint32_t)(32 * p.lda);
     d.step_b = (uint32_t)p.ldb;
-    d.lds_a = gemm::lds_addr(g_lds_a) + 4096u * w;
+    d.lds_a = gemm::lds_addr(g_lds_a) + 16384u * (w >> 2) + 1024u * (w & 3);
     d.lds_b = gemm::lds_addr(g_lds_b) + 4096u * w;
     d.lds_s = gemm::lds_addr(g_lds_sa) + 256u * (w & 3);
     const int nbs = (p.n + 127) / 128;
@@ -183,12 +209,14 @@ __device__ inline void block_dma_one(const BlockDma& d, int j, int stage, int kb
     if (j < 4) {
         v4u r = d.ra;
         r.z = live ? r.z : 0u;
-        dma16_so(d.lds_a + stage * kTileBytes + 1024 * j, d.va[j & 1], r, k0 + (uint32_t)(j >> 1) * d.step_a);
+        const uint32_t va = j ? add_lane_offset(d.va, (uint32_t)j * d.step_a) : d.va;
+        dma16_so(d.lds_a + stage * kTileBytes + 4096 * j, va, r, k0);
     } else if (j < 8) {
         const int jb = j - 4;
         v4u r = d.rb;
         r.z = live ? r.z : 0u;
-        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, d.vb[jb & 1], r, k0 + (uint32_t)(jb >> 1) * d.step_b);
+        const uint32_t vb = (jb >> 1) ? add_lane_offset(d.vb[jb & 1], d.step_b) : d.vb[jb & 1];
+        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, vb, r, k0);
     } else {
         v4u r = d.rs;
         r.z = live ? r.z : 0u;
@@ -236,10 +264,11 @@ __device__ inline void block_codes(int kb, int w)
 // A fragment i = s/4 and B fragment j = s%4, then promotes the result of
 // slot s - 3.  Reads run one fragment group ahead.  At slot 1 the waves meet
 // once every wave holds this block's B fragments: the B half of this
-// block's stage then takes the B DMA of block kb + 2.  After the block's last
-// A fragment read (slot 24) every wave waits for its DMA of the next block
-// and meets the others at the barrier of slot 26, after which the A half is
-// free for block kb + 2 and the next block's data is visible.
+// block's stage then takes the B DMA of block kb + 2.  The barrier of slot
+// 10 releases the rows of A fragment groups 0-3 for their half of A.  After
+// the block's last A fragment read (slot 24) every wave waits for its DMA of
+// the next block and meets the others at the barrier of slot 26, after which
+// groups 4-7 take the other half and the next block's data is visible.
 // MODE kModeE8M0: the scales are powers of two; each MFMA applies them
 // itself (per-lane E8M0 code of its A row, the N block's code for B) and
 // accumulates in place, with no promotion.  MODE kModeTensor: one scale per
@@ -347,21 +376,26 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             // factors of group i + 1: group i - 1's last promotion (slot 4 i - 1) ran at slot 4 i + 2
             if (PROMOTE && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
             if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
-            // B of block kb + 2 early in the block: this block's B fragments are
-            // already in registers once every wave has passed the barrier of
-            // slot 1, so the stage's B half is free; A follows at slot 26, after
-            // the block's last A read.  The delivery of the two halves is spread
-            // over the block, and B is requested almost two blocks ahead.
-            if (s == 1) gemm::barrier_lds();
+            // Block kb + 2 into this block's stage, as its parts are released.
+            // B early in the block: this block's B fragments are in registers
+            // once every wave has passed the barrier of slot 1, so the stage's
+            // B half is free.  A in two halves: the rows of fragment groups
+            // 0-3 are free once every wave has read group 3 (slot 8), those of
+            // groups 4-7 after the block's last A read (slot 24), so the halves
+            // go out after the barriers of slots 10 and 26.  The requests
+            // reach the memory system spread over the block (a split into four
+            // parts, with a third barrier, measured no faster).
+            if (s == 1 || s == 10) gemm::barrier_lds();
             if (s >= 2 && s <= 5) block_dma_one(d, 4 + (s - 2), t & 1, kb + 2, 0, live2);
+            if (s == 10) block_dma_one(d, 0, t & 1, kb + 2, 0, live2);
+            if (s == 11) block_dma_one(d, 1, t & 1, kb + 2, 0, live2);
             if (s == 26) {
-                // everything but this block's 4 B instructions (loads complete in order)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                // all but the 6 instructions of block kb + 2 issued in this block
+                // (loads complete in order): block kb + 1 and the scales of kb + 2
+                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
                 gemm::barrier_lds();
-            }
-            if (s >= 26 && s <= 27) {
-                block_dma_one(d, 2 * (s - 26), t & 1, kb + 2, 0, live2);
-                block_dma_one(d, 2 * (s - 26) + 1, t & 1, kb + 2, 0, live2);
+                block_dma_one(d, 2, t & 1, kb + 2, 0, live2);
+                block_dma_one(d, 3, t & 1, kb + 2, 0, live2);
             }
             if (s == 30) block_dma_one(d, 8, 0, 0, kb + 3, live3);   // s_a of block kb + 3
             if (s == 27) {
@@ -520,12 +554,14 @@ __device__ inline void item_dma_ab(const BlockDma& d, const ItemDesc& e, int j, 
     if (j < 4) {
         v4u r = e.ra;
         r.z = live ? r.z : 0u;
-        dma16_so(d.lds_a + stage * kTileBytes + 1024 * j, d.va[j & 1], r, k0 + (uint32_t)(j >> 1) * d.step_a);
+        const uint32_t va = j ? add_lane_offset(d.va, (uint32_t)j * d.step_a) : d.va;
+        dma16_so(d.lds_a + stage * kTileBytes + 4096 * j, va, r, k0);
     } else {
         const int jb = j - 4;
         v4u r = e.rb;
         r.z = live ? r.z : 0u;
-        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, d.vb[jb & 1], r, k0 + (uint32_t)(jb >> 1) * d.step_b);
+        const uint32_t vb = (jb >> 1) ? add_lane_offset(d.vb[jb & 1], d.step_b) : d.vb[jb & 1];
+        dma16_so(d.lds_b + stage * kTileBytes + 1024 * jb, vb, r, k0);
     }
 }
 
@@ -548,7 +584,8 @@ __device__ inline void item_dma_scales(const KArgs& p, const BlockDma& d, const 
 // blocks runs during the current tile's last blocks and its epilogue.  LDS
 // stages and rings are indexed by the position u in the stream; one DMA
 // cursor runs two positions ahead, fetching each position's scales (slot 2)
-// before its B half (slots 2-5) and A half (slots 26-27).  Launched only
+// before its B half (slots 2-5) and A in two halves (slots 10-11 and 26).
+// Launched only
 // when every output row segment can be stored whole (fast_store).
 template <int FA, int FB, int MODE>
 __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
@@ -645,18 +682,21 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
             }
             if (PROMOTE && j == 3) fc[(i + 1) & 1] = *reinterpret_cast<const v4f*>(i < 7 ? lf + 16 * (i + 1) : lf_next);
             if (i == 7) bf[j] = gemm::load_frag(lb_next, wn + 16 * j);
-            if (s == 1) gemm::barrier_lds();
+            // the DMA schedule of k_gemm_block (B at slots 2-5, A's halves
+            // after the barriers of slots 10 and 26)
+            if (s == 1 || s == 10) gemm::barrier_lds();
             if (s == 2) item_dma_scales(p, dl, de, u + 2, kb2, live2);
             if (s >= 2 && s <= 5) item_dma_ab(dl, de, 4 + (s - 2), u & 1, kb2, live2);
+            if (s == 10) item_dma_ab(dl, de, 0, u & 1, kb2, live2);
+            if (s == 11) item_dma_ab(dl, de, 1, u & 1, kb2, live2);
             if (s == 26) {
-                // all but this block's 4 B instructions (loads complete in order;
-                // an epilogue's stores before them are waited for too)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                // all but the 6 A/B instructions issued in this block (loads
+                // complete in order; an epilogue's stores before them are
+                // waited for too)
+                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
                 gemm::barrier_lds();
-            }
-            if (s >= 26 && s <= 27) {
-                item_dma_ab(dl, de, 2 * (s - 26), u & 1, kb2, live2);
-                item_dma_ab(dl, de, 2 * (s - 26) + 1, u & 1, kb2, live2);
+                item_dma_ab(dl, de, 2, u & 1, kb2, live2);
+                item_dma_ab(dl, de, 3, u & 1, kb2, live2);
             }
             if (s == 27) {
                 if constexpr (E8M0)
