@@ -288,7 +288,8 @@ fp8_status fp8_quantize_scaled_mm(const void* x, int64_t ldx, fp8_format fa, flo
  * out when it has none) and one cast pass over all of its caches, TENSOR
  * caches with the scale of their amax pass, BLOCK caches with each block's
  * own amax.  An empty TENSOR cache gets scale 1 from a launch of its own.
- * The result is byte-identical to fp8_quantize(master, FROM_AMAX) of each,
+ * A call with one cache runs fp8_quantize's kernels for it (as many
+ * launches, the faster tile kernels).  The result is byte-identical to fp8_quantize(master, FROM_AMAX) of each,
  * counters included.  rows and cols below 2^31.  masters[i] is a
  * device pointer, master_dtypes[i] its dtype; the three arrays are HOST arrays
  * of length count.  Workspace: fp8_requant_workspace_size(). */
