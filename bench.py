@@ -367,8 +367,13 @@ def other_workloads(torch, fm, synth, np, dev):
     xs1 = torch.empty(1, dtype=torch.float32, device=dev)
     ws1 = torch.empty(1, dtype=torch.float32, device=dev)
     y1 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    fq_x = lambda: fm.quantize(x1, fm.E4M3, scale=xs1, out=xq1)
-    fq_w = lambda: fm.quantize(w1, fm.E4M3, scale=ws1, out=wq1)
+    # workspaces allocated once, as a training loop would hold them
+    wsx1 = torch.empty(max(fm.lib().fp8_quantize_workspace_size(m, k, fm.TENSOR, fm.FROM_AMAX), 1),
+                       dtype=torch.uint8, device=dev)
+    wsw1 = torch.empty(max(fm.lib().fp8_quantize_workspace_size(n, k, fm.TENSOR, fm.FROM_AMAX), 1),
+                       dtype=torch.uint8, device=dev)
+    fq_x = lambda: fm.quantize(x1, fm.E4M3, scale=xs1, out=xq1, workspace=wsx1)
+    fq_w = lambda: fm.quantize(w1, fm.E4M3, scale=ws1, out=wq1, workspace=wsw1)
     fg = lambda: fm.scaled_mm(xq1, fm.E4M3, xs1, fm.TENSOR, wq1, fm.E4M3, ws1, fm.TENSOR, out=y1)
     for _ in range(20):
         fq_x(), fq_w(), fg()

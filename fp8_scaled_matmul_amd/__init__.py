@@ -296,8 +296,11 @@ def amax(x, gran: int = TENSOR):
 
 
 def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scale=None,
-             want_t: bool = False, counters: Counters | None = None, out=None, out_t=None):
-    """Returns (q uint8 [rows, cols], q_t uint8 [cols, rows] or None, scale fp32)."""
+             want_t: bool = False, counters: Counters | None = None, out=None, out_t=None, workspace=None):
+    """Returns (q uint8 [rows, cols], q_t uint8 [cols, rows] or None, scale fp32).
+    workspace: optional uint8 device tensor of at least
+    fp8_quantize_workspace_size(rows, cols, gran, mode) bytes (allocated per
+    call when not given)."""
     torch = _torch()
     _check_tensor(x, "x", (torch.bfloat16, torch.float32), unit_col_stride=True)
     rows, cols = x.shape
@@ -312,19 +315,23 @@ def quantize(x, fmt: int = E4M3, gran: int = TENSOR, mode: int = FROM_AMAX, scal
         _check_tensor(out_t, "out_t", (torch.uint8,), (cols, rows), unit_col_stride=True)
     if out_t is not None and not want_t:
         raise ValueError("out_t given without want_t=True")
-    _check_devices(x, scale, out, out_t, counters.buf if counters else None)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", (torch.uint8,), contiguous=True)
+    _check_devices(x, scale, out, out_t, workspace, counters.buf if counters else None)
+    wsb = lib().fp8_quantize_workspace_size(rows, cols, gran, mode)
+    if workspace is not None and workspace.numel() < wsb:
+        raise ValueError(f"workspace needs {wsb} bytes, got {workspace.numel()}")
     if scale is None:
         scale = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
     q = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     qt = None
     if want_t:
         qt = out_t if out_t is not None else torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
-    wsb = lib().fp8_quantize_workspace_size(rows, cols, gran, mode)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
     check(fp8_quantize(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), fmt, gran, mode,
                        scale.data_ptr(), q.data_ptr(), _ld(q),
                        _ptr(qt), _ld(qt) if qt is not None else 0,
-                       counters.ptr() if counters else None, ws.data_ptr(), wsb, _stream()))
+                       counters.ptr() if counters else None, ws.data_ptr(), ws.numel(), _stream()))
     return q, qt, scale
 
 

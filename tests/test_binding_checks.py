@@ -70,6 +70,8 @@ def test_quantize_rejects():
         fm.quantize(x, fm.E4M3, out_t=_u8(384, 256))
     with pytest.raises(ValueError, match="GIVEN"):
         fm.quantize(x, fm.E4M3, mode=fm.GIVEN)
+    with pytest.raises(ValueError, match="workspace must"):
+        fm.quantize(x, fm.E4M3, workspace=torch.empty(64, dtype=torch.float32))
     with pytest.raises(ValueError, match="CUDA"):
         fm.quantize(x, fm.E4M3, fm.BLOCK_128x128, scale=_f32(2, 3), out=_u8(256, 384),
                     want_t=True, out_t=_u8(384, 256))

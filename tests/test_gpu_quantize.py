@@ -262,3 +262,17 @@ def test_amax_quotient_just_above_fmax(fmt):
         blk = np.ascontiguousarray(x[:, 128 * j:128 * (j + 1)])
         c = _cmp(blk, fmt, fm.TENSOR, want_t=True)
         assert c["saturated"] == 0
+
+
+def test_caller_workspace():
+    """A workspace held by the caller gives the same bytes as a per-call one;
+    one that is too small is rejected before any launch."""
+    x = synth.with_outliers_bf16(14, (300, 520), frac=0.01)
+    xd = dev_bf16(x)
+    q1, _, s1 = fm.quantize(xd, fm.E4M3)
+    wsb = fm.lib().fp8_quantize_workspace_size(300, 520, fm.TENSOR, fm.FROM_AMAX)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q2, _, s2 = fm.quantize(xd, fm.E4M3, workspace=ws)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    with pytest.raises(ValueError, match="workspace needs"):
+        fm.quantize(xd, fm.E4M3, workspace=ws[: wsb - 1])
