@@ -12,7 +12,7 @@ import pytest
 import fp8_scaled_matmul_amd as fm
 import oracle
 import synth
-from gpu_util import assert_gemm_close, dev_f32, dev_u8, host
+from gpu_util import assert_gemm_close, dev_bf16, dev_f32, dev_u8, host
 
 pytestmark = pytest.mark.gpu
 PAIRS = [(fm.E4M3, fm.E4M3), (fm.E5M2, fm.E4M3), (fm.E4M3, fm.E5M2), (fm.E5M2, fm.E5M2)]
@@ -48,6 +48,33 @@ def _codes(fmt, seed, shape, sigma):
     return q, s
 
 
+def _k768_cases():
+    g = np.random.default_rng(20240613)
+    return [(i, int(g.integers(1, 3000)), 4 * int(g.integers(1, 700))) for i in range(12)]
+
+
+@pytest.mark.parametrize("i,m,n", _k768_cases())
+def test_k768_random_shapes(i, m, n):
+    """K = 768 (the A-stationary kernel): the per-tensor GEMM on FP8 codes,
+    and the forward with X quantized inside it (codes, transposed codes and
+    scale bit-exact, y within tolerance), ragged panels and column units."""
+    fa, fb = PAIRS[i % 4]
+    k = 768
+    x = synth.normal_bf16(3000 + i, 0, (m, k), 1.0)
+    a, at, sa, _ = oracle.quantize(x, fa, want_t=True)
+    b, sb = _codes(fb, 4000 + i, (n, k), 0.02)
+    ref = oracle.gemm(a, fa, sa, oracle.TENSOR, b, fb, sb, oracle.TENSOR)
+    what = f"k768 case {i}: {m}x{n} formats {fa},{fb}"
+    y = fm.scaled_mm(dev_u8(a), fa, dev_f32(np.float32(sa).reshape(1)), fm.TENSOR,
+                     dev_u8(b), fb, dev_f32(np.float32(sb).reshape(1)), fm.TENSOR)
+    assert_gemm_close(host(y), ref, what)
+    y2, s2, q2, qt2 = fm.quantize_scaled_mm(dev_bf16(x), fa, dev_u8(b), fb, dev_f32(np.float32(sb).reshape(1)),
+                                            want_q=True, want_t=True)
+    assert_gemm_close(host(y2), ref, what + " fused")
+    assert host(s2)[0] == np.float32(sa).reshape(-1)[0], what + " fused scale"
+    assert np.array_equal(host(q2), a) and np.array_equal(host(qt2), at), what + " fused codes"
+
+
 @pytest.mark.parametrize("i,m,n,k", _tensor_cases())
 def test_tensor_scaled_random_shapes(i, m, n, k):
     fa, fb = PAIRS[i % 4]
@@ -75,7 +102,7 @@ def test_block_scaled_random_shapes(i, m, n, k):
 
 
 # ------------------------------------------------------------------ quantizers
-from gpu_util import dev_bf16, gpu_quantize, same_counters  # noqa: E402
+from gpu_util import gpu_quantize, same_counters  # noqa: E402
 
 
 def _quant_cases():
@@ -92,7 +119,8 @@ def test_quantize_random_shapes(i, rows, cols):
     fmt = (fm.E4M3, fm.E5M2)[i % 2]
     x = synth.channel_scaled_bf16(400 + i, 0, 5, (rows, cols))
     xd = dev_bf16(x)
-    for gran, want_t in ((fm.TENSOR, False), (fm.TENSOR, True), (fm.ROW_1x128, False), (fm.BLOCK_128x128, True)):
+    for gran, want_t in ((fm.TENSOR, False), (fm.TENSOR, True), (fm.ROW_1x128, False), (fm.BLOCK_128x128, True),
+                         (fm.BLOCK_128x128, False)):
         q, qt, s, c = gpu_quantize(xd, fmt, gran, fm.FROM_AMAX, None, want_t)
         oq, oqt, os_, oc = oracle.quantize(x, fmt, gran, oracle.FROM_AMAX, None, want_t)
         what = f"case {i}: {rows}x{cols} format {fmt} granularity {gran} transposed {want_t}"
