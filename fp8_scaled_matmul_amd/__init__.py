@@ -179,7 +179,13 @@ def _torch():
 
 
 def _stream():
+    """The current HIP stream of the current device, as an integer handle.
+    torch's raw-stream query is used when it exists (it skips building a
+    Stream object, about 3 us per call on the host)."""
     torch = _torch()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
     return torch.cuda.current_stream().cuda_stream
 
 
