@@ -485,22 +485,39 @@ class WeightCache:
                                self.counters.ptr() if self.counters else None)
 
 
+class RequantPlan:
+    """A prepared refresh of a fixed list of caches from a fixed list of
+    masters: the argument checks, the descriptor array and the workspace are
+    set up once, and each call is one C call (the refresh after every
+    optimizer step of a training loop).  The masters and caches are held by
+    reference; their storage must stay where it is."""
+
+    def __init__(self, caches: list[WeightCache], masters: list):
+        torch = _torch()
+        if len(caches) != len(masters):
+            raise ValueError("one master per cache")
+        for c, m in zip(caches, masters):
+            _check_tensor(m, "master", (torch.bfloat16, torch.float32), (c.rows, c.cols), contiguous=True)
+        if caches:
+            _check_devices(*masters, *[c.q for c in caches])
+        self.caches, self.masters = list(caches), list(masters)
+        n = len(caches)
+        self._n = n
+        self._descs = (WeightCacheDesc * max(n, 1))(*[c.desc() for c in caches])
+        self._masters = (ctypes.c_void_p * max(n, 1))(*[m.data_ptr() for m in masters])
+        self._dtypes = (ctypes.c_int * max(n, 1))(*[_dtype_code(m) for m in masters])
+        self._wsb = lib().fp8_requant_workspace_size(self._descs, n) if n else 0
+        self._ws = torch.empty(max(self._wsb, 1), dtype=torch.uint8,
+                               device=masters[0].device if n else "cpu")
+
+    def __call__(self) -> None:
+        if self._n:
+            check(lib().fp8_requant_weights(self._descs, self._masters, self._dtypes, self._n,
+                                            self._ws.data_ptr(), self._wsb, _stream()))
+
+
 def requant_weights(caches: list[WeightCache], masters: list) -> None:
     """Refresh every cache from its master in one call."""
-    torch = _torch()
     if not caches:
         return
-    if len(caches) != len(masters):
-        raise ValueError("one master per cache")
-    for c, m in zip(caches, masters):
-        _check_tensor(m, "master", (torch.bfloat16, torch.float32), (c.rows, c.cols), contiguous=True)
-    _check_devices(*masters, *[c.q for c in caches])
-    descs = [c.desc() for c in caches]
-    arr = (WeightCacheDesc * len(descs))(*descs)
-    wsb = lib().fp8_requant_workspace_size(arr, len(descs))
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=masters[0].device)
-    for c, m in zip(caches, masters):
-        if tuple(m.shape) != (c.rows, c.cols) or not m.is_contiguous():
-            raise ValueError("master must be contiguous with the cache's shape")
-    check(fp8_requant_weights(descs, [m.data_ptr() for m in masters], [_dtype_code(m) for m in masters],
-                              ws.data_ptr(), wsb, _stream()))
+    RequantPlan(caches, masters)()

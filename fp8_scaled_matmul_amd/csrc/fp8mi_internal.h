@@ -54,6 +54,7 @@ struct RequantItem {
     int32_t wg0, nwg;       // per-tensor: its amax workgroups (one partial key each)
     int8_t dtype, fmt, gran;
     int8_t vec_amax, vec_tile;
+    int8_t lean;            // bf16 with 16-byte rows: whole tiles go to the 512-thread tile kernel
 };
 constexpr int kRequantMaxCaches = 24;    // caches per launch (kernel-argument size)
 constexpr int kRequantAmaxParts = 256;   // at most this many partial keys per cache

@@ -1223,6 +1223,11 @@ __global__ void __launch_bounds__(kThreads) k_requant_cast(RequantBatch bt)
         }
         const RequantItem& it = bt.item[c];
         const int64_t tid = f - it.tile0;
+        if (it.lean) {
+            // whole tiles of a lean cache were cast by k_requant_lean
+            const int64_t tc = (it.cols + kTile - 1) / kTile, br = tid / tc, bc = tid - br * tc;
+            if ((br + 1) * kTile <= it.rows && (bc + 1) * kTile <= it.cols) continue;
+        }
         if (it.fmt == FP8_E4M3) {
             if (it.dtype == FP8_IN_BF16) requant_tile<0, 0>(it, s, special, tid, tile, sat, und, nan);
             else requant_tile<0, 1>(it, s, special, tid, tile, sat, und, nan);
@@ -1233,6 +1238,134 @@ __global__ void __launch_bounds__(kThreads) k_requant_cast(RequantBatch bt)
         __syncthreads();   // the LDS staging tile and the block amax scratch are reused by the next tile
     }
     if (c >= 0) flush_counters_block(bt.item[c].ctr, sat, und, nan);
+}
+
+// Whole bf16 tiles of the batch's lean caches, one tile per 512-thread
+// workgroup (the arrangement of k_tile128t_bf16 and k_block128_bf16: 4 x 8
+// elements per thread, at most 64 registers, so that a launch of up to 4
+// tiles per CU is resident at once; the 12 caches of a 12-layer model's
+// up-projection are 1728 tiles).  Per-tensor caches take their scale from
+// their amax partials, per-block caches each block's own amax.  Edge tiles,
+// and every tile of a cache that is not lean, return at once and are left to
+// k_requant_cast.
+template <int FMT>
+__device__ __forceinline__ void requant_lean_tile(const RequantItem& it, int64_t tid, int64_t tiles_c, uint32_t* tl,
+                                                  uint32_t* sh)
+{
+    const int t = threadIdx.x, g = t >> 4, k = t & 15;
+    const int64_t br = tid / tiles_c, bc = tid - br * tiles_c;
+    const int64_t r0 = br * kTile, c0 = bc * kTile;
+    const int64_t ld = it.cols;
+    const uint16_t* x = static_cast<const uint16_t*>(it.x);
+    uint4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = ld_stream(x + (r0 + 4 * g + i) * ld + c0 + 8 * k);
+    float s;
+    bool fast;
+    if (it.gran == FP8_TENSOR) {
+        const uint32_t kk = reduce_partials(it.parts, it.nwg);
+        s = scale_from_amax<FMT>(key_amax(kk));
+        fast = !key_special(kk) && s >= kCorrectedQuotMinScale;
+        if (tid == 0 && t == 0) it.scale[0] = s;
+    } else {
+        us2 pk = us2{0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk = pkmax8(pk, w[i]);
+        uint32_t key = wave_max(pk_raw(pk));
+        if ((t & 63) == 0) sh[t >> 6] = key;
+        __syncthreads();
+        key = sh[0];
+#pragma unroll
+        for (int i = 1; i < kBlkThreads / 64; ++i) key = max(key, sh[i]);
+        if (key >= kRawNonFinite) {
+            // an Inf or NaN in the block: the exact merge (finite amax + flag)
+            __syncthreads();
+            uint32_t e = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
+                    e = key_merge(e, absbits_bf16(ws[h] >> 16));
+                }
+            }
+            e = wave_key_merge(e);
+            if ((t & 63) == 0) sh[t >> 6] = e;
+            __syncthreads();
+            key = sh[0];
+            for (int i = 1; i < kBlkThreads / 64; ++i) key = key_merge(key, sh[i]);
+        }
+        s = scale_from_amax<FMT>(key_amax(key));
+        fast = !key_special(key) && s >= kCorrectedQuotMinScale;
+        if (t == 0) it.scale[br * tiles_c + bc] = s;
+    }
+    const float r = 1.0f / s;
+    uint32_t sat = 0, und = 0, nan = 0;
+    uint2 code[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        if (fast) {
+            code[i] = cast8_bf16_fast<FMT>(ws, s, r, und);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[2 * h] = bf16_lo(ws[h]);
+                v[2 * h + 1] = bf16_hi(ws[h]);
+            }
+            code[i] = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+        }
+        *reinterpret_cast<uint2*>(it.q + (r0 + 4 * g + i) * ld + c0 + 8 * k) = code[i];
+    }
+    if (it.qt) {
+        // the transposed copy through LDS, as in k_tile128t_bf16
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t a = half ? code[0].y : code[0].x;
+            const uint32_t b = half ? code[1].y : code[1].x;
+            const uint32_t c = half ? code[2].y : code[2].x;
+            const uint32_t d = half ? code[3].y : code[3].x;
+            const uint32_t x0 = __builtin_amdgcn_perm(b, a, 0x05010400u);
+            const uint32_t x1 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+            const uint32_t y0 = __builtin_amdgcn_perm(d, c, 0x05010400u);
+            const uint32_t y1 = __builtin_amdgcn_perm(d, c, 0x07030602u);
+            const uint32_t col[4] = {__builtin_amdgcn_perm(y0, x0, 0x05040100u), __builtin_amdgcn_perm(y0, x0, 0x07060302u),
+                                     __builtin_amdgcn_perm(y1, x1, 0x05040100u), __builtin_amdgcn_perm(y1, x1, 0x07060302u)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tl[(8 * k + 4 * half + j) * 32 + (g ^ (4 * (k & 7)))] = col[j];
+        }
+        barrier_lds_only();
+        const int cc = t & 127, qq = t >> 7;
+        const int sw = 4 * ((cc >> 3) & 7);
+        const uint4 lo = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq) ^ sw)]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq + 4) ^ sw)]);
+        uint8_t* dst = it.qt + (c0 + cc) * (int64_t)it.rows + r0 + 32 * qq;
+        *reinterpret_cast<uint4*>(dst) = lo;
+        *reinterpret_cast<uint4*>(dst + 16) = hi;
+    }
+    flush_counters_block(it.ctr, sat, und, nan);
+}
+
+__global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(8))) k_requant_lean(RequantBatch bt)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t tl[kTile * kTile / 4];
+    __shared__ uint32_t sh[kBlkThreads / 64];
+    const int64_t f = blockIdx.x;
+    int c = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (f >= bt.item[i].tile0) c = i;
+    const RequantItem& it = bt.item[c];
+    if (!it.lean) return;
+    const int64_t tiles_c = (it.cols + kTile - 1) / kTile;
+    const int64_t tid = f - it.tile0;
+    const int64_t br = tid / tiles_c, bc = tid - br * tiles_c;
+    if ((br + 1) * kTile > it.rows || (bc + 1) * kTile > it.cols) return;   // edge tile
+    if (it.fmt == FP8_E4M3)
+        requant_lean_tile<0>(it, tid, tiles_c, tl, sh);
+    else
+        requant_lean_tile<1>(it, tid, tiles_c, tl, sh);
 }
 
 __global__ void k_counters_reset(fp8_counters* ctr)
@@ -1450,9 +1583,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)
 }
 
 // Weight-cache refresh: the caches go in groups of kRequantMaxCaches; per
-// group one amax launch over its per-tensor caches (if any) and one cast
-// launch over all of its caches.  Empty caches take launch_quantize (a
-// per-tensor one still reports scale 1).
+// group one amax launch over its per-tensor caches (if any), one launch for
+// the whole tiles of its bf16 caches (k_requant_lean) and one for every other
+// tile (k_requant_cast, left out when there is none).  Empty caches take
+// launch_quantize (a per-tensor one still reports scale 1).
 hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream)
 {
     hipError_t e;
@@ -1462,7 +1596,8 @@ hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream
     for (int g0 = 0; g0 < count; g0 += kRequantMaxCaches) {
         RequantBatch bt{};
         int wg = 0;
-        int64_t tiles = 0;
+        int64_t tiles = 0, rest = 0;
+        bool any_lean = false;
         for (int i = g0; i < std::min(count, g0 + kRequantMaxCaches); ++i) {
             const QuantArgs& a = caches[i];
             if (a.rows == 0 || a.cols == 0) {
@@ -1485,8 +1620,13 @@ hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream
             it.vec_amax = aligned16(a.x);
             it.vec_tile = aligned16(a.x) && aligned16(a.q) && (!a.qt || aligned16(a.qt)) && (a.cols * eb) % 16 == 0 &&
                           a.cols % 8 == 0 && (!a.qt || a.rows % 16 == 0);
+            it.lean = a.dtype == FP8_IN_BF16 && it.vec_tile;
             it.tile0 = tiles;
             tiles += cdiv(a.rows, kTile) * cdiv(a.cols, kTile);
+            // tiles left to the general kernel
+            rest += it.lean ? cdiv(a.rows, kTile) * cdiv(a.cols, kTile) - (a.rows / kTile) * (a.cols / kTile)
+                            : cdiv(a.rows, kTile) * cdiv(a.cols, kTile);
+            any_lean |= it.lean && a.rows >= kTile && a.cols >= kTile;
             it.wg0 = wg;
             it.nwg = 0;
             if (a.gran == FP8_TENSOR) {
@@ -1501,9 +1641,21 @@ hipError_t launch_requant(const QuantArgs* caches, int count, hipStream_t stream
             hipLaunchKernelGGL(k_requant_amax, dim3(wg), dim3(kThreads), 0, stream, bt);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        const int grid = (int)std::min<int64_t>(tiles, (int64_t)num_cus() * 4);
-        hipLaunchKernelGGL(k_requant_cast, dim3(grid), dim3(kThreads), 0, stream, bt);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (any_lean && tiles > INT32_MAX) {
+            // more tiles than one grid dimension holds: the general kernel takes all
+            for (int i = 0; i < bt.count; ++i) bt.item[i].lean = 0;
+            any_lean = false;
+            rest = tiles;
+        }
+        if (any_lean) {
+            hipLaunchKernelGGL(k_requant_lean, dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream, bt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (rest > 0) {
+            const int grid = (int)std::min<int64_t>(tiles, (int64_t)num_cus() * 4);
+            hipLaunchKernelGGL(k_requant_cast, dim3(grid), dim3(kThreads), 0, stream, bt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

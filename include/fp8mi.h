@@ -284,10 +284,11 @@ fp8_status fp8_quantize_scaled_mm(const void* x, int64_t ldx, fp8_format fa, flo
  *   ctr         optional counters.
  * fp8_requant_weights() re-quantizes every cache from its master with a
  * fresh amax scale (current scaling).  The caches go in groups of up to 24;
- * each group takes two launches: one amax pass over its TENSOR caches (left
- * out when it has none) and one cast pass over all of its caches, TENSOR
- * caches with the scale of their amax pass, BLOCK caches with each block's
- * own amax.  An empty TENSOR cache gets scale 1 from a launch of its own.
+ * each group takes at most three launches: one amax pass over its TENSOR
+ * caches (left out when it has none), one cast pass over the whole tiles of
+ * its bf16 caches and one over every other tile (left out when there is
+ * none), TENSOR caches with the scale of their amax pass, BLOCK caches with
+ * each block's own amax.  An empty TENSOR cache gets scale 1 from a launch of its own.
  * A call with one cache runs fp8_quantize's kernels for it (as many
  * launches, the faster tile kernels).  The result is byte-identical to fp8_quantize(master, FROM_AMAX) of each,
  * counters included.  rows and cols below 2^31.  masters[i] is a

@@ -146,11 +146,16 @@ def test_twelve_layer_refresh():
     ws = [synth.normal_bf16(70 + l, 1, (3072, 768), 0.02) for l in range(12)]
     caches = [fm.WeightCache(3072, 768, with_t=True) for _ in ws]
     masters = [dev_bf16(w) for w in ws]
-    fm.requant_weights(caches, masters)
+    # a prepared plan, called after each update of the masters in place
+    plan = fm.RequantPlan(caches, masters)
+    plan()
+    for l, (c, w) in enumerate(zip(caches, ws)):
+        oq, _, os_, _ = oracle.requant(w, fm.E4M3)
+        assert np.array_equal(host(c.q), oq) and host(c.scale)[0] == os_[0], f"layer {l}, first refresh"
     ws2 = [synth.apply_update_bf16(w, synth.update_noise_f32(70 + l, w.shape)) for l, w in enumerate(ws)]
     for m, w2 in zip(masters, ws2):
         m.copy_(dev_bf16(w2))
-    fm.requant_weights(caches, masters)
+    plan()
     for l, (c, w2) in enumerate(zip(caches, ws2)):
         oq, oqt, os_, _ = oracle.requant(w2, fm.E4M3)
         assert np.array_equal(host(c.q), oq) and np.array_equal(host(c.q_t), oqt), f"layer {l}"
