@@ -92,9 +92,10 @@ struct GemmArgs {
     fp8_counters* ctr;
 };
 
-// A-stationary per-tensor GEMM (gemm_astat.hip): K is one model width, the
-// whole [192, K] panel of A codes stays in LDS.  A is FP8 codes, or bf16
-// quantized on the way in with the amax scale of `partials`.
+// A-stationary per-tensor GEMM (gemm_astat.hip): K is one model width, a
+// whole panel of A codes ([208, K], or [192, K] when cast from bf16) stays
+// in LDS.  A is FP8 codes, or bf16 quantized on the way in with the amax
+// scale of `partials`.
 constexpr int kAstatK = 768;
 struct AstatArgs {
     const void* a;

@@ -9,16 +9,17 @@
 //
 // Design (gfx950: 160 KB of LDS per CU, 256 CUs, L2-to-CU delivery about
 // 21 bytes per clock per CU):
-//   - a workgroup of 4 waves keeps a whole 192 x 768 panel of A codes
-//     (144 KB) in LDS and walks the output columns in units of 256; only B
+//   - a workgroup of 4 waves keeps a whole 208 x 768 panel of A codes
+//     (156 KB; 192 rows when it casts bf16 A) in LDS and walks the output
+//     columns in units of 256; only B
 //     streams from L2, straight into each wave's registers (each wave owns
 //     64 columns, so no B byte is fetched twice per CU).  Per 128-deep K step
-//     a CU moves 32 KB of B for 12.6 MFLOP: 384 flops per byte, against 256
-//     for a 256 x 256 tile that stages both operands;
-//   - every unit is 6 K steps of 48 v_mfma_f32_16x16x128_f8f6f4 per wave
-//     (12 A fragments from LDS x 4 B fragments); B is fetched two K steps
+//     a CU moves 32 KB of B for 13.6 MFLOP: 416 flops per byte (384 with
+//     192 rows), against 256 for a 256 x 256 tile that stages both operands;
+//   - every unit is 6 K steps of 52 v_mfma_f32_16x16x128_f8f6f4 per wave
+//     (13 A fragments from LDS x 4 B fragments); B is fetched two K steps
 //     ahead, across unit boundaries;
-//   - one accumulator set (192 AGPRs); the epilogue (scale, bf16, 8-byte
+//   - one accumulator set (208 AGPRs); the epilogue (scale, bf16, 8-byte
 //     stores of four adjacent columns) trails the last K step's MFMAs by one
 //     fragment, so the matrix pipe does not wait for it;
 //   - workgroups are persistent over contiguous unit ranges (units in panel
@@ -40,19 +41,33 @@ using gemm::v4f;
 using gemm::v4u;
 using gemm::v8i;
 
-constexpr int kAsRows = 192;                 // rows of A held in LDS
-constexpr int kAsFrags = kAsRows / 16;       // 16-row MFMA fragments per panel
 constexpr int kAsN = 256;                    // output columns per unit (64 per wave)
 constexpr int kBF = 4;                       // B fragments per wave and K step
 constexpr int kAsKB = kAstatK / 128;         // 128-deep MFMA steps per unit
 constexpr int kAsChunks = kAstatK / 16;      // 16-byte chunks per panel row
-constexpr int kAsPanelBytes = kAsRows * kAstatK;
 constexpr int kAsThreads = 256;
 // B fragments are requested kBAhead K steps before use, into a ring of
 // kBRing steps (a unit's K steps are a multiple of it, so ring slots are
 // fixed at compile time): 64 KB of B in flight per CU.
 constexpr int kBRing = 3, kBAhead = 2;
 static_assert(kAstatK / 128 % kBRing == 0 && kBAhead < kBRing, "B ring");
+
+// The A panel held in LDS: 208 rows (13 fragments, 156 KB) of FP8 codes, or
+// 192 rows (12 fragments) when it is cast from bf16 A.  Measured on the
+// 65536 x 3072 forward: 208 rows run 6-8% faster than 192 (8% fewer B bytes
+// per flop, and 3792 units spread over 256 CUs as 14-15 each instead of 4104
+// as 16-17); the cast form ran 2% slower with them.  A fragments are read
+// from LDS `ahead` steps before use, into a ring of `ring` slots (a unit's
+// 6 x frags steps are a multiple of it).
+template <int ASRC>
+struct Panel {
+    static constexpr int rows = ASRC ? 192 : 208;
+    static constexpr int frags = rows / 16;
+    static constexpr int bytes = rows * kAstatK;
+    static constexpr int ahead = 3, ring = ASRC ? 4 : 6;
+    static_assert(kAsKB * frags % ring == 0 && ahead < ring, "A ring");
+};
+constexpr int kAsMinRows = Panel<1>::rows, kAsMaxBytes = Panel<0>::bytes;
 
 struct AsArgs {
     const void* a;          // FP8 codes [m, k] (lda bytes) or bf16 [m, k] (lda elements)
@@ -76,7 +91,7 @@ struct AsArgs {
     fp8_counters* ctr;
 };
 
-__shared__ __attribute__((aligned(1024))) uint8_t s_panel[kAsPanelBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_panel[kAsMaxBytes];
 __shared__ uint32_t s_red[kAsThreads / 64];
 
 // 16-byte chunk lc of panel row r sits at chunk lc ^ (r % 16) of the row
@@ -162,7 +177,8 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 // soffset.  mx keeps the running maximum of the stored |bf16| patterns
 // (>= 0x7F80: an Inf or NaN was written; counted exactly at the end, see
 // recount()).
-__device__ inline void store_frag(const v4f (&acc)[kAsFrags][kBF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
+template <int NF>
+__device__ inline void store_frag(const v4f (&acc)[NF][kBF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
                                   int rows, uint32_t row_bytes, float scale, us2& mx)
 {
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -178,7 +194,7 @@ __device__ inline void store_frag(const v4f (&acc)[kAsFrags][kBF], int i, __amdg
     }
 }
 
-// The panel of rows m0 .. m0 + 191 into LDS.  FP8 A: the codes are copied.
+// The panel of rows m0 .. m0 + Panel::rows - 1 into LDS.  FP8 A: the codes are copied.
 // bf16 A: each 16-element chunk is cast with the scale (the corrected
 // quotient when `fast`, IEEE division otherwise, exactly as fp8_quantize
 // does), and, when `own`, its codes go to xq and its events are counted.
@@ -186,21 +202,23 @@ template <int FA, int ASRC>
 __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p, int m0, bool own, float s, float rcp, bool fast, uint32_t& sat,
                                   uint32_t& und, uint32_t& nan)
 {
-    const int rows = min(kAsRows, p.m - m0);
+    using P = Panel<ASRC>;
+    const int rows = min(P::rows, p.m - m0);
     const int t = threadIdx.x;
-    constexpr int per = kAsRows * kAsChunks / kAsThreads;   // 36 chunks per thread
+    constexpr int per = P::rows * kAsChunks / kAsThreads;   // chunks per thread
     constexpr int batch = 4;
     if constexpr (ASRC == 0) {
         // LDS DMA: instruction j of wave w fills panel bytes
-        // [1024 (36 w + j), +1024); lane l's 16 bytes land at offset 16 l,
+        // [1024 (per_wave w + j), +1024); lane l's 16 bytes land at offset 16 l,
         // which is chunk pc = (P % 768) / 16 of row r = P / 768 (P the byte
         // position), so the lane fetches logical chunk pc ^ (r % 16).  All
-        // 36 requests of a wave are in flight at once; rows past m read as
+        // requests of a wave are in flight at once; rows past m read as
         // zeros (range-checked descriptor).
         const v4u ra = gemm::make_rsrc(static_cast<const uint8_t*>(p.a) + (int64_t)m0 * p.lda, (uint32_t)(rows * p.lda));
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
         const uint32_t lds0 = gemm::lds_addr(s_panel);
-        constexpr int per_wave = kAsPanelBytes / 1024 / (kAsThreads / 64);   // 36
+        constexpr int per_wave = P::bytes / 1024 / (kAsThreads / 64);
+        static_assert(P::bytes % (1024 * (kAsThreads / 64)) == 0, "panel DMA");
 #pragma unroll 4
         for (int j = 0; j < per_wave; ++j) {
             const int slot = per_wave * w + j;
@@ -221,6 +239,7 @@ __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p
         const uint32_t row_x = (uint32_t)(p.lda * 2);
         if (fast) {
             // the corrected quotient (bf16 input, finite tensor, s >= 2^-64)
+            static_assert(per % batch == 0, "cast batches");
             uint32_t u_loc = 0;
 #pragma unroll 1
             for (int j0 = 0; j0 < per; j0 += batch) {
@@ -289,8 +308,9 @@ __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p
 // with consecutive row quads write consecutive 4-byte words of a q_t row.
 __device__ __attribute__((always_inline)) inline void store_panel_t(const AsArgs& p, int m0)
 {
-    const int rows = min(kAsRows, p.m - m0);
-    constexpr int rq_n = kAsRows / 4, kq_n = kAstatK / 4;
+    using P = Panel<1>;
+    const int rows = min(P::rows, p.m - m0);
+    constexpr int rq_n = P::rows / 4, kq_n = kAstatK / 4;
 #pragma unroll 1
     for (int b = threadIdx.x; b < rq_n * kq_n; b += kAsThreads) {
         const int rq = b % rq_n, kq = b / rq_n;
@@ -322,16 +342,18 @@ __device__ __attribute__((always_inline)) inline void store_panel_t(const AsArgs
 
 // Exact count of the non-finite outputs this lane stored for units
 // u0 .. u1 - 1 (only run when one was seen: reads the outputs back).
+template <int ASRC>
 __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& p, int u0, int u1)
 {
+    using P = Panel<ASRC>;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t n = 0;
     for (int u = u0; u < u1; ++u) {
-        const int m0 = (u / p.ntn) * kAsRows, n0 = (u % p.ntn) * kAsN;
+        const int m0 = (u / p.ntn) * P::rows, n0 = (u % p.ntn) * kAsN;
         const int col = n0 + 64 * w + 4 * (l & 15);
         if (col >= p.n) continue;
-        for (int i = 0; i < kAsFrags; ++i)
+        for (int i = 0; i < P::frags; ++i)
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * i + 4 * (l >> 4) + r;
                 if (row >= p.m) continue;
@@ -342,13 +364,14 @@ __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& 
     return n;
 }
 
-// One unit is 72 fragment steps (K step kb = s / 12, A fragment i = s % 12):
-// four MFMAs on A fragment i and the K step's four B fragments; the A
-// fragment of step s + 3 is read from LDS (a ring of four); at i == 0 the B
-// fragments of K step kb + 2 are requested (into the next unit at the end).
-// One accumulator set: in the last K step, fragment i - 1 (final once its
-// last MFMA, issued one step earlier, has run) is scaled, rounded and stored
-// at step i, and fragment 11 at the next unit's first step, after that
+// One unit is 6 F fragment steps, F = Panel::frags (K step kb = s / F, A
+// fragment i = s % F): four MFMAs on A fragment i and the K step's four B
+// fragments; the A fragment of step s + 3 is read from LDS (into the ring);
+// at i == 0 the B fragments of K step kb + 2 are requested (into the next
+// unit at the end).  One accumulator set: in the last K step, fragment
+// i - 1 (final once its last MFMA, issued one step earlier, has run) is
+// scaled, rounded and stored at step i, and fragment F - 1 at the next
+// unit's first step, after that
 // step's MFMAs (which write fragment 0); a fragment is overwritten by the
 // next unit only after it has been read out.  A scheduling barrier closes
 // every step (and separates its MFMAs from its read-out).
@@ -382,9 +405,11 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     uint32_t sat = 0, und = 0, nan = 0;
     us2 mx = us2{0, 0};
 
-    v4f acc[kAsFrags][kBF];
+    using P = Panel<ASRC>;
+    constexpr int kF = P::frags;
+    v4f acc[kF][kBF];
     v8i bb[kBRing][kBF];
-    v8i af[4];
+    v8i af[P::ring];
     const AFragBase ab = a_frag_base();
     uint32_t boff[kBF];
 #pragma unroll
@@ -393,11 +418,11 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     __amdgpu_buffer_rsrc_t rs_cur = b_rsrc(p, u0, u1), rs_next = b_rsrc(p, u0 + 1, u1);
 
     int panel_loaded = -1;
-    bool pending = false;   // fragment 11 of the previous unit not stored yet
+    bool pending = false;   // fragment kF - 1 of the previous unit not stored yet
     int pm0 = 0, pn0 = 0;
 
     auto out_rsrc = [&](int m0) {
-        return gemm::make_store_rsrc(p.c + (int64_t)m0 * p.ldc, (uint32_t)(min(kAsRows, p.m - m0) * p.ldc * 2));
+        return gemm::make_store_rsrc(p.c + (int64_t)m0 * p.ldc, (uint32_t)(min(P::rows, p.m - m0) * p.ldc * 2));
     };
     // the lane's store offset within a unit's rows: its columns and row group
     // (n % 4 == 0: a column group is inside the matrix or past it entirely)
@@ -408,10 +433,10 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
 
     for (int u = u0; u < u1; ++u) {
         const int panel = u / p.ntn, nt = u - panel * p.ntn;
-        const int m0 = panel * kAsRows, n0 = nt * kAsN;
+        const int m0 = panel * P::rows, n0 = nt * kAsN;
         if (panel != panel_loaded) {
             if (pending) {
-                store_frag(acc, kAsFrags - 1, out_rsrc(pm0), col_off(pn0), min(kAsRows, p.m - pm0), row_bytes,
+                store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes,
                            out_scale, mx);
                 pending = false;
             }
@@ -434,14 +459,14 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         }
         const __amdgpu_buffer_rsrc_t rc_prev = out_rsrc(pm0);
         const uint32_t co_prev = col_off(pn0);
-        const int rows_prev = min(kAsRows, p.m - pm0);
+        const int rows_prev = min(P::rows, p.m - pm0);
         const __amdgpu_buffer_rsrc_t rc = out_rsrc(m0);
         const uint32_t co = col_off(n0);
-        const int rows = min(kAsRows, p.m - m0);
+        const int rows = min(P::rows, p.m - m0);
         const bool drain = pending;
 #pragma unroll
-        for (int s = 0; s < kAsKB * kAsFrags; ++s) {
-            const int kb = s / kAsFrags, i = s % kAsFrags;
+        for (int s = 0; s < kAsKB * kF; ++s) {
+            const int kb = s / kF, i = s % kF;
             if (i == 0) {
                 const int kf = kb + kBAhead;
 #pragma unroll
@@ -450,15 +475,15 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
             }
             // A fragment of step s + 3 (wrapping to the next unit's first K step)
             {
-                const int s3 = (s + 3) % (kAsKB * kAsFrags);
-                af[(s + 3) & 3] = a_frag(ab, s3 % kAsFrags, s3 / kAsFrags);
+                const int s3 = (s + P::ahead) % (kAsKB * kF);
+                af[(s + P::ahead) % P::ring] = a_frag(ab, s3 % kF, s3 / kF);
             }
-            const v8i& a = af[s & 3];
+            const v8i& a = af[s % P::ring];
 #pragma unroll
             for (int f = 0; f < kBF; ++f)
                 acc[i][f] = gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
             __builtin_amdgcn_sched_barrier(0);
-            if (s == 0 && drain) store_frag(acc, kAsFrags - 1, rc_prev, co_prev, rows_prev, row_bytes, out_scale, mx);
+            if (s == 0 && drain) store_frag(acc, kF - 1, rc_prev, co_prev, rows_prev, row_bytes, out_scale, mx);
             if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, rows, row_bytes, out_scale, mx);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -469,8 +494,8 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         rs_next = b_rsrc(p, u + 2, u1);
     }
     if (pending)
-        store_frag(acc, kAsFrags - 1, out_rsrc(pm0), col_off(pn0), min(kAsRows, p.m - pm0), row_bytes, out_scale, mx);
-    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount(p, u0, u1) : 0u;
+        store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
+    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ASRC>(p, u0, u1) : 0u;
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
     if constexpr (ASRC == 1) flush_counters_block(p.ctr, sat, und, nan);
 }
@@ -481,7 +506,7 @@ bool astat_supported(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, 
 {
     return k == kAstatK && m > 0 && n > 0 && n % 4 == 0 && ldc % 4 == 0 &&
            (reinterpret_cast<uintptr_t>(c) & 7u) == 0 && lda < ((int64_t)1 << 22) && ldb < ((int64_t)1 << 22) &&
-           ldc < ((int64_t)1 << 21) && (m + kAsRows - 1) / kAsRows * ((n + kAsN - 1) / kAsN) < ((int64_t)1 << 31);
+           ldc < ((int64_t)1 << 21) && (m + kAsMinRows - 1) / kAsMinRows * ((n + kAsN - 1) / kAsN) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream)
@@ -506,7 +531,8 @@ hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream
     p.c = static_cast<uint16_t*>(g.c);
     p.ldc = g.ldc;
     p.ctr = g.ctr;
-    const int panels = (int)((g.m + kAsRows - 1) / kAsRows);
+    const int rows = g.bf16_a ? Panel<1>::rows : Panel<0>::rows;
+    const int panels = (int)((g.m + rows - 1) / rows);
     // n == 0 still walks one (empty) column unit per panel, so that the
     // panel's codes and counters are produced
     p.ntn = std::max(1, (int)((g.n + kAsN - 1) / kAsN));

@@ -143,16 +143,29 @@ def test_fused_speedrun_forward_full():
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
-@pytest.mark.parametrize("m,n", [(1, 8), (191, 16), (193, 136), (1000, 264), (2500, 1024), (300, 260), (64, 258)])
+@pytest.mark.parametrize("m,n", [(1, 8), (191, 16), (193, 136), (207, 24), (208, 256), (209, 260), (417, 132),
+                                 (1000, 264), (2500, 1024), (300, 260), (64, 258)])
 def test_scaled_mm_k768_shapes(fa, fb, m, n):
     """fp8_scaled_mm with per-tensor scales and K = 768 (the A-stationary
-    kernel): ragged panels and column units, every format pair."""
+    kernel, 208-row panels of codes): ragged panels and column units, every
+    format pair."""
     g = np.random.default_rng(m * 3 + n)
     a = synth.f32_to_bf16_bits((g.standard_normal((m, K))).astype(np.float32))
     aq, _, sa, _ = oracle.quantize(a, fa)
     bq, sb = _wcodes(fb, n, 2 * m + n)
     y = host(fm.scaled_mm(dev_u8(aq), fa, dev_f32(sa), fm.TENSOR, dev_u8(bq), fb, dev_f32(sb), fm.TENSOR))
     assert_gemm_close(y, oracle.gemm(aq, fa, sa, 0, bq, fb, sb, 0), f"k768 {fa}x{fb} {m}x{n}")
+
+
+def test_scaled_mm_k768_units_spanning_panels():
+    """More column units than workgroups (units of one panel split between
+    two workgroups, which both load it): A [8000, 768] with 0.1% outliers,
+    E4M3 x E4M3, every output element against the oracle."""
+    x = synth.with_outliers_bf16(604, (8000, K))
+    aq, _, sa, _ = oracle.quantize(x, fm.E4M3)
+    bq, sb = _wcodes(fm.E4M3, 3072, 13)
+    y = host(fm.scaled_mm(dev_u8(aq), 0, dev_f32(sa), 0, dev_u8(bq), 0, dev_f32(sb), 0))
+    assert_gemm_close(y, oracle.gemm(aq, 0, sa, 0, bq, 0, sb, 0), "k768 8000x3072")
 
 
 def test_scaled_mm_k768_strided_and_odd_n():
