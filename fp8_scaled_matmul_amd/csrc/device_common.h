@@ -37,6 +37,9 @@ template <> struct Fmt<1> {
 // Scales at or above this use the multiply + correction quotient; smaller
 // ones take a full IEEE division (see quot_corrected).
 constexpr float kCorrectedQuotMinScale = 0x1p-64f;
+// A given scale (no amax bounds x) takes the corrected quotient only up to
+// this (1/s stays a normal number), and only for |x| <= given_limit(s).
+constexpr float kCorrectedQuotMaxScale = 0x1p64f;
 
 // Dequantization scale from an amax: s = fl32(amax / fmax), 1 for amax 0,
 // raised to FLT_MIN when smaller (so no result depends on denormal scales).
@@ -85,6 +88,33 @@ __device__ inline float quot_corrected(float x, float s, float r)
     float e = __builtin_fmaf(-q0, s, x);
     float v = __builtin_fmaf(e, r, q0);
     return __builtin_copysignf(v, x);
+}
+
+// Given scale s: the largest bf16 magnitude pattern L (0 .. 0x7F7F) whose
+// IEEE quotient L / s is at most fmax; for s outside [2^-64, 2^64], 0.  Every
+// bf16 x with |x| <= L then has a finite quotient within +-fmax, on which
+// the corrected quotient gives the IEEE quotient's code and events (checked
+// on the CPU over every x and s significand, and against a scan of every
+// magnitude for over 6000 scales), and nothing saturates.  Elements above L
+// (saturating, Inf, NaN) take IEEE division.  L starts from fl32(fmax s) cut
+// to bf16 and moves at most one step: up when the next magnitude's quotient
+// still rounds to fmax or below, else down when its own does not (the one
+// below is then always within: a bf16 step is 2^-8 of it, fl32(fmax s) is
+// within 2^-24 of fmax s).  Every returned L has been checked with a
+// division, except after a step down, which is safe by that margin.
+template <int FMT>
+__device__ inline uint32_t given_limit(float s)
+{
+    if (!(s >= kCorrectedQuotMinScale && s <= kCorrectedQuotMaxScale)) return 0;
+    constexpr float fm = Fmt<FMT>::fmax;
+    uint32_t c = __builtin_bit_cast(uint32_t, fm * s) >> 16;
+    c = c > 0x7F7Fu ? 0x7F7Fu : c;
+    auto within = [&](uint32_t b) { return __builtin_bit_cast(float, b << 16) / s <= fm; };
+    if (c < 0x7F7Fu && within(c + 1))
+        ++c;
+    else if (!within(c))
+        --c;
+    return c;
 }
 
 // Two fp32 values (already clamped to +-fmax) to two FP8 bytes; hi selects

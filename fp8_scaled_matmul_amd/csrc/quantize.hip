@@ -263,10 +263,11 @@ __global__ void __launch_bounds__(kThreads) k_delayed_record(const uint32_t* par
 // Pass 2 of per-tensor scaling (or the whole job with a given scale): every
 // workgroup rebuilds the amax from the partials, derives s, and streams its
 // share of x -> q.  16 elements (32 B of bf16 in, 16 B out) per vector.
-template <int FMT, int DT, bool FAST>
+// This form divides (IEEE) and keeps every counter: fp32 input, non-finite
+// tensors, scales outside the corrected quotient's range.
+template <int FMT, int DT>
 __device__ inline void cast_stream(const void* x, int64_t rows, int64_t cols, int64_t ld, int vec,
-                                   uint8_t* q, int64_t ldq, float s, float r, uint32_t& sat,
-                                   uint32_t& und, uint32_t& nan)
+                                   uint8_t* q, int64_t ldq, float s, uint32_t& sat, uint32_t& und, uint32_t& nan)
 {
     const int64_t nvec = vec ? cols / 16 : 0;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -280,10 +281,10 @@ __device__ inline void cast_stream(const void* x, int64_t rows, int64_t cols, in
             load8<DT>(x, xb + i * 16 + 8, b, dummy);
             load8<DT>(x, xb + (i + stride) * 16, c, dummy);
             load8<DT>(x, xb + (i + stride) * 16 + 8, d, dummy);
-            const uint2 oa = cast8<FMT, FAST>(a, s, r, sat, und, nan);
-            const uint2 ob = cast8<FMT, FAST>(b, s, r, sat, und, nan);
-            const uint2 oc = cast8<FMT, FAST>(c, s, r, sat, und, nan);
-            const uint2 od = cast8<FMT, FAST>(d, s, r, sat, und, nan);
+            const uint2 oa = cast8<FMT, false>(a, s, 0.0f, sat, und, nan);
+            const uint2 ob = cast8<FMT, false>(b, s, 0.0f, sat, und, nan);
+            const uint2 oc = cast8<FMT, false>(c, s, 0.0f, sat, und, nan);
+            const uint2 od = cast8<FMT, false>(d, s, 0.0f, sat, und, nan);
             *reinterpret_cast<uint4*>(q + qb + i * 16) = make_uint4(oa.x, oa.y, ob.x, ob.y);
             *reinterpret_cast<uint4*>(q + qb + (i + stride) * 16) = make_uint4(oc.x, oc.y, od.x, od.y);
         }
@@ -292,13 +293,61 @@ __device__ inline void cast_stream(const void* x, int64_t rows, int64_t cols, in
             uint32_t dummy = 0;
             load8<DT>(x, xb + i * 16, a, dummy);
             load8<DT>(x, xb + i * 16 + 8, b, dummy);
-            const uint2 oa = cast8<FMT, FAST>(a, s, r, sat, und, nan);
-            const uint2 ob = cast8<FMT, FAST>(b, s, r, sat, und, nan);
+            const uint2 oa = cast8<FMT, false>(a, s, 0.0f, sat, und, nan);
+            const uint2 ob = cast8<FMT, false>(b, s, 0.0f, sat, und, nan);
             *reinterpret_cast<uint4*>(q + qb + i * 16) = make_uint4(oa.x, oa.y, ob.x, ob.y);
         }
         for (int64_t c = nvec * 16 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride) {
             uint32_t dummy = 0;
-            q[qb + c] = cast1<FMT, FAST>(load1<DT>(x, xb + c, dummy), s, r, sat, und, nan);
+            q[qb + c] = cast1<FMT, false>(load1<DT>(x, xb + c, dummy), s, 0.0f, sat, und, nan);
+        }
+    }
+}
+
+// The same stream for bf16 input on the corrected quotient.  PATH 1: the
+// scale comes from the tensor's amax (every element qualifies).  PATH 2: a
+// given scale; a group of 8 takes the corrected quotient when each |x| is at
+// most lim = given_limit(s), else IEEE division and every counter.
+template <int FMT, int PATH>
+__device__ inline void cast_stream_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int vec,
+                                        uint8_t* q, int64_t ldq, float s, float r, uint32_t lim, uint32_t& sat,
+                                        uint32_t& und, uint32_t& nan)
+{
+    auto cast = [&](const uint4& w) -> uint2 {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        if constexpr (PATH == 2) {
+            const us2 m = pkmax8(us2{0, 0}, w);
+            if ((uint32_t)(m.x > m.y ? m.x : m.y) > lim) {
+                float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                              bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                return cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+            }
+        }
+        return cast8_bf16_fast<FMT>(ws, s, r, und);
+    };
+    const int64_t nvec = vec ? cols / 16 : 0;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const uint16_t* xr = x + row * ld;
+        uint8_t* qr = q + row * ldq;
+        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        for (; i + stride < nvec; i += 2 * stride) {
+            const uint4 a = ld_stream(xr + i * 16), b = ld_stream(xr + i * 16 + 8);
+            const uint4 c = ld_stream(xr + (i + stride) * 16), d = ld_stream(xr + (i + stride) * 16 + 8);
+            const uint2 oa = cast(a), ob = cast(b), oc = cast(c), od = cast(d);
+            *reinterpret_cast<uint4*>(qr + i * 16) = make_uint4(oa.x, oa.y, ob.x, ob.y);
+            *reinterpret_cast<uint4*>(qr + (i + stride) * 16) = make_uint4(oc.x, oc.y, od.x, od.y);
+        }
+        for (; i < nvec; i += stride) {
+            const uint4 a = ld_stream(xr + i * 16), b = ld_stream(xr + i * 16 + 8);
+            const uint2 oa = cast(a), ob = cast(b);
+            *reinterpret_cast<uint4*>(qr + i * 16) = make_uint4(oa.x, oa.y, ob.x, ob.y);
+        }
+        for (int64_t c = nvec * 16 + (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cols; c += stride) {
+            const uint32_t h = xr[c];
+            const float xv = __builtin_bit_cast(float, h << 16);
+            qr[c] = (PATH == 1 || (h & 0x7FFFu) <= lim) ? cast1<FMT, true>(xv, s, r, sat, und, nan)
+                                                        : cast1<FMT, false>(xv, s, 0.0f, sat, und, nan);
         }
     }
 }
@@ -320,13 +369,19 @@ __global__ void __launch_bounds__(kThreads) k_cast_tensor(const void* x, int64_t
         s = scale[0];
     }
     uint32_t sat = 0, und = 0, nan = 0;
-    const bool fast = DT == 0 && partials && !special && s >= kCorrectedQuotMinScale;
-    if (fast) {
-        const float r = 1.0f / s;
-        cast_stream<FMT, DT, true>(x, rows, cols, ld, vec, q, ldq, s, r, sat, und, nan);
-    } else {
-        cast_stream<FMT, DT, false>(x, rows, cols, ld, vec, q, ldq, s, 0.0f, sat, und, nan);
+    bool general = true;
+    if constexpr (DT == 0) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (partials && !special && s >= kCorrectedQuotMinScale) {
+            cast_stream_bf16<FMT, 1>(xb, rows, cols, ld, vec, q, ldq, s, 1.0f / s, 0, sat, und, nan);
+            general = false;
+        } else if (!partials && s >= kCorrectedQuotMinScale && s <= kCorrectedQuotMaxScale) {
+            cast_stream_bf16<FMT, 2>(xb, rows, cols, ld, vec, q, ldq, s, 1.0f / s, given_limit<FMT>(s), sat, und,
+                                     nan);
+            general = false;
+        }
     }
+    if (general) cast_stream<FMT, DT>(x, rows, cols, ld, vec, q, ldq, s, sat, und, nan);
     flush_counters_block(ctr, sat, und, nan);
 }
 
@@ -575,6 +630,9 @@ __global__ void __launch_bounds__(kThreads)
             s_tensor = scale[0];
         }
     }
+    // a given per-tensor scale: the corrected quotient for the threads whose
+    // elements all have |x| <= given_limit(s) (mode 2 takes it per block)
+    const uint32_t lim_tensor = SCALE_MODE == 0 && !partials ? given_limit<FMT>(s_tensor) : 0u;
     uint32_t sat = 0, und = 0, nan = 0;
 
     auto load = [&](int64_t id, uint4 (&w)[8]) {
@@ -597,7 +655,14 @@ __global__ void __launch_bounds__(kThreads)
         bool fast;
         if constexpr (SCALE_MODE == 0) {
             s = s_tensor;
-            fast = partials && !special_tensor && s >= kCorrectedQuotMinScale;
+            if (partials) {
+                fast = !special_tensor && s >= kCorrectedQuotMinScale;
+            } else {
+                us2 m = us2{0, 0};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = pkmax8(m, cur[i]);
+                fast = (uint32_t)(m.x > m.y ? m.x : m.y) <= lim_tensor;   // per thread
+            }
         } else if constexpr (SCALE_MODE == 1) {
             us2 m = us2{0, 0};
 #pragma unroll
@@ -633,7 +698,10 @@ __global__ void __launch_bounds__(kThreads)
             fast = hist_fast && (uint32_t)(m.x > m.y ? m.x : m.y) <= hist_bits;   // per thread
         } else {
             s = scale[(r0 / kTile) * tiles_c_all + c0 / kTile];
-            fast = false;
+            us2 m = us2{0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = pkmax8(m, cur[i]);
+            fast = (uint32_t)(m.x > m.y ? m.x : m.y) <= given_limit<FMT>(s);   // per thread
         }
 
         uint8_t* qrow = q + (r0 + 8 * g) * ldq + c0 + 8 * k;

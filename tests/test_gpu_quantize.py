@@ -13,7 +13,10 @@ from gpu_util import dev_bf16, dev_f32, gpu_quantize, host, same_counters
 pytestmark = pytest.mark.gpu
 FMTS = [fm.E4M3, fm.E5M2]
 SCALES = [1.0, 2.0 ** -10, 0.5, 3.0, 1.0 / 448.0, 1.0 / 57344.0, 4.5 / 448.0, 5000.0 / 448.0,
-          5000.0 / 57344.0, 0.0213 / 448.0, 1.1920929e-7, 7.3e-3, 1e-30, 3e30]
+          5000.0 / 57344.0, 0.0213 / 448.0, 1.1920929e-7, 7.3e-3, 1e-30, 3e30,
+          # arbitrary significands, and the ends of the corrected quotient's range
+          # for a given scale ([2^-64, 2^64]) with a step beyond each
+          0.7853982, 1.9999999, 2.0 ** -64, 2.0 ** -64 * 0.99999994, 2.0 ** 64, 2.0 ** 64 * 1.0000001]
 
 
 def _cmp(x_bits, fmt, gran, mode=fm.FROM_AMAX, scale=None, want_t=False, x_dev=None, x_orc=None):
@@ -35,6 +38,25 @@ def test_every_bf16_pattern_given_scale(fmt, s):
     x = synth.all_bf16_patterns()
     _cmp(x, fmt, fm.TENSOR, fm.GIVEN, np.float32([s]))
     _cmp(x, fmt, fm.TENSOR, fm.GIVEN, np.float32([s]), want_t=True)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("gran", [fm.TENSOR, fm.BLOCK_128x128])
+def test_given_scale_saturating_outliers(fmt, gran):
+    """A given scale (or per-block scales) below amax / fmax on a tensor
+    with 1% outliers of 500-5000: elements past the scale's limit saturate
+    and are counted, the rest take the corrected quotient; codes, transposed
+    codes and counters bit-exact.  Whole tiles and ragged edges."""
+    x = synth.with_outliers_bf16(7, (1000, 1408), frac=0.01)
+    g = np.random.default_rng(8)
+    if gran == fm.TENSOR:
+        sc = np.float32([(200.0 if fmt == fm.E4M3 else 0.05) * g.uniform(0.5, 2.0)]) / np.float32(448.0)
+    else:
+        sc = (g.uniform(0.2, 2.0, size=oracle.scale_shape(2, *x.shape)) *
+              (1.0 if fmt == fm.E4M3 else 0.001)).astype(np.float32)
+    c = _cmp(x, fmt, gran, fm.GIVEN, sc)
+    _cmp(x, fmt, gran, fm.GIVEN, sc, want_t=True)
+    assert c["saturated"] > 0
 
 
 @pytest.mark.parametrize("fmt", FMTS)
