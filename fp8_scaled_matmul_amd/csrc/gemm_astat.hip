@@ -56,18 +56,25 @@ static_assert(kAstatK / 128 % kBRing == 0 && kBAhead < kBRing, "B ring");
 // 192 rows (12 fragments) when it is cast from bf16 A.  Measured on the
 // 65536 x 3072 forward: 208 rows run 6-8% faster than 192 (8% fewer B bytes
 // per flop, and 3792 units spread over 256 CUs as 14-15 each instead of 4104
-// as 16-17); the cast form ran 2% slower with them.  A fragments are read
-// from LDS `ahead` steps before use, into a ring of `ring` slots (a unit's
-// 6 x frags steps are a multiple of it).
-template <int ASRC>
+// as 16-17); the cast form ran 2% slower with them.  Short A (every unit of
+// 32-row panels fits in one round of workgroups) takes 32-row panels: one
+// unit per workgroup, whose time is then its B stream rather than the load
+// of a 156 KB panel.  A fragments are read from LDS `ahead` steps before
+// use, into a ring of `ring` slots (a unit's 6 x frags steps are a multiple
+// of it).
+constexpr int kAsRowsCodes = 208, kAsRowsCast = 192, kAsRowsShort = 32;
+template <int ROWS>
 struct Panel {
-    static constexpr int rows = ASRC ? 192 : 208;
+    static constexpr int rows = ROWS;
     static constexpr int frags = rows / 16;
     static constexpr int bytes = rows * kAstatK;
-    static constexpr int ahead = 3, ring = ASRC ? 4 : 6;
-    static_assert(kAsKB * frags % ring == 0 && ahead < ring, "A ring");
+    static constexpr int ahead = 3, ring = kAsKB * frags % 4 == 0 ? 4 : 6;
+    static_assert(rows % 16 == 0 && kAsKB * frags % ring == 0 && ahead < ring, "A ring");
+    // the next unit's first MFMAs (fragment 0) run before the previous
+    // unit's last fragment is stored
+    static_assert(frags >= 2, "panel of at least two fragments");
 };
-constexpr int kAsMinRows = Panel<1>::rows, kAsMaxBytes = Panel<0>::bytes;
+constexpr int kAsMinRows = kAsRowsShort, kAsMaxBytes = Panel<kAsRowsCodes>::bytes;
 
 struct AsArgs {
     const void* a;          // FP8 codes [m, k] (lda bytes) or bf16 [m, k] (lda elements)
@@ -198,11 +205,11 @@ __device__ inline void store_frag(const v4f (&acc)[NF][kBF], int i, __amdgpu_buf
 // bf16 A: each 16-element chunk is cast with the scale (the corrected
 // quotient when `fast`, IEEE division otherwise, exactly as fp8_quantize
 // does), and, when `own`, its codes go to xq and its events are counted.
-template <int FA, int ASRC>
+template <int FA, int ASRC, int ROWS>
 __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p, int m0, bool own, float s, float rcp, bool fast, uint32_t& sat,
                                   uint32_t& und, uint32_t& nan)
 {
-    using P = Panel<ASRC>;
+    using P = Panel<ROWS>;
     const int rows = min(P::rows, p.m - m0);
     const int t = threadIdx.x;
     constexpr int per = P::rows * kAsChunks / kAsThreads;   // chunks per thread
@@ -308,7 +315,7 @@ __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p
 // with consecutive row quads write consecutive 4-byte words of a q_t row.
 __device__ __attribute__((always_inline)) inline void store_panel_t(const AsArgs& p, int m0)
 {
-    using P = Panel<1>;
+    using P = Panel<kAsRowsCast>;
     const int rows = min(P::rows, p.m - m0);
     constexpr int rq_n = P::rows / 4, kq_n = kAstatK / 4;
 #pragma unroll 1
@@ -342,10 +349,10 @@ __device__ __attribute__((always_inline)) inline void store_panel_t(const AsArgs
 
 // Exact count of the non-finite outputs this lane stored for units
 // u0 .. u1 - 1 (only run when one was seen: reads the outputs back).
-template <int ASRC>
+template <int ROWS>
 __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& p, int u0, int u1)
 {
-    using P = Panel<ASRC>;
+    using P = Panel<ROWS>;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t n = 0;
@@ -375,7 +382,7 @@ __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& 
 // step's MFMAs (which write fragment 0); a fragment is overwritten by the
 // next unit only after it has been read out.  A scheduling barrier closes
 // every step (and separates its MFMAs from its read-out).
-template <int FA, int FB, int ASRC>
+template <int FA, int FB, int ASRC, int ROWS>
 __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
 {
     // unit range of this workgroup: ranges of one XCD (workgroups b = x mod 8)
@@ -405,7 +412,8 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     uint32_t sat = 0, und = 0, nan = 0;
     us2 mx = us2{0, 0};
 
-    using P = Panel<ASRC>;
+    static_assert(ASRC == 0 || ROWS == kAsRowsCast, "panel of the cast form");
+    using P = Panel<ROWS>;
     constexpr int kF = P::frags;
     v4f acc[kF][kBF];
     v8i bb[kBRing][kBF];
@@ -442,16 +450,15 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
             }
             __syncthreads();   // every wave is done with the previous panel
             const bool own = ASRC == 1 && nt == 0;
-            load_panel<FA, ASRC>(p, m0, own, sa, rcp, fast, sat, und, nan);
+            load_panel<FA, ASRC, ROWS>(p, m0, own, sa, rcp, fast, sat, und, nan);
             __syncthreads();
             if (ASRC == 1 && own && p.xqt) store_panel_t(p, m0);
             panel_loaded = panel;
             // the first A fragments of the panel (the same for every unit of
             // it), and this unit's first B steps again: the B ring is left
             // dead across the panel load, whose loads then have its registers
-            af[0] = a_frag(ab, 0, 0);
-            af[1] = a_frag(ab, 1, 0);
-            af[2] = a_frag(ab, 2, 0);
+#pragma unroll
+            for (int j = 0; j < P::ahead; ++j) af[j] = a_frag(ab, j % kF, j / kF);
 #pragma unroll
             for (int kb = 0; kb < kBAhead; ++kb)
 #pragma unroll
@@ -495,7 +502,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     }
     if (pending)
         store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
-    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ASRC>(p, u0, u1) : 0u;
+    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ROWS>(p, u0, u1) : 0u;
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
     if constexpr (ASRC == 1) flush_counters_block(p.ctr, sat, und, nan);
 }
@@ -531,21 +538,28 @@ hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream
     p.c = static_cast<uint16_t*>(g.c);
     p.ldc = g.ldc;
     p.ctr = g.ctr;
-    const int rows = g.bf16_a ? Panel<1>::rows : Panel<0>::rows;
-    const int panels = (int)((g.m + rows - 1) / rows);
     // n == 0 still walks one (empty) column unit per panel, so that the
     // panel's codes and counters are produced
     p.ntn = std::max(1, (int)((g.n + kAsN - 1) / kAsN));
+    // panel form: 0 codes (208 rows), 1 cast from bf16 (192), 2 short A (32)
+    int form = g.bf16_a ? 1 : 0;
+    if (!g.bf16_a && (g.m + kAsRowsShort - 1) / kAsRowsShort * p.ntn <= num_cus) form = 2;
+    const int rows = form == 1 ? kAsRowsCast : form == 2 ? kAsRowsShort : kAsRowsCodes;
+    const int panels = (int)((g.m + rows - 1) / rows);
     p.units = panels * p.ntn;
     const int grid = std::min(p.units, num_cus);
-    const int sel = (g.fa * 2 + g.fb) * 2 + (g.bf16_a ? 1 : 0);
+    const int sel = (g.fa * 2 + g.fb) * 3 + form;
     switch (sel) {
-#define FP8MI_ASTAT(FA_, FB_, S_)                                                                     \
-    case (FA_ * 2 + FB_) * 2 + S_:                                                                    \
-        hipLaunchKernelGGL((k_gemm_astat<FA_, FB_, S_>), dim3(grid), dim3(kAsThreads), 0, stream, p); \
+#define FP8MI_ASTAT(FA_, FB_, F_, S_, R_)                                                                \
+    case (FA_ * 2 + FB_) * 3 + F_:                                                                       \
+        hipLaunchKernelGGL((k_gemm_astat<FA_, FB_, S_, R_>), dim3(grid), dim3(kAsThreads), 0, stream, p); \
         break;
-        FP8MI_ASTAT(0, 0, 0) FP8MI_ASTAT(0, 0, 1) FP8MI_ASTAT(0, 1, 0) FP8MI_ASTAT(0, 1, 1)
-        FP8MI_ASTAT(1, 0, 0) FP8MI_ASTAT(1, 0, 1) FP8MI_ASTAT(1, 1, 0) FP8MI_ASTAT(1, 1, 1)
+#define FP8MI_ASTAT3(FA_, FB_)                       \
+    FP8MI_ASTAT(FA_, FB_, 0, 0, kAsRowsCodes)        \
+    FP8MI_ASTAT(FA_, FB_, 1, 1, kAsRowsCast)         \
+    FP8MI_ASTAT(FA_, FB_, 2, 0, kAsRowsShort)
+        FP8MI_ASTAT3(0, 0) FP8MI_ASTAT3(0, 1) FP8MI_ASTAT3(1, 0) FP8MI_ASTAT3(1, 1)
+#undef FP8MI_ASTAT3
 #undef FP8MI_ASTAT
     }
     return hipGetLastError();
