@@ -10,8 +10,14 @@
 
 namespace fp8mi {
 
-// Number of per-workgroup partial maxima the per-tensor amax pass writes.
+// Room for the per-workgroup partial maxima of a per-tensor amax pass (the
+// workspace size), and the workgroups the pass runs on at most.  Measured on
+// 8192 x 8192 with the last-level cache flushed, per-tensor quantize from
+// amax: 512 workgroups 64.9 us, 1024 66.0 us, 2048 67.8 us; the step's X and
+// dY quantizations were the same with all three.
 constexpr int kAmaxPartials = 2048;
+constexpr int kAmaxGrid = 512;
+static_assert(kAmaxGrid <= kAmaxPartials, "amax grid");
 constexpr size_t kAmaxWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
 
 // Library-owned scratch of fp8_quantize_noalloc: room for the amax partials

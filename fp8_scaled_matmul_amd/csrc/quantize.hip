@@ -1548,7 +1548,7 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
             int64_t r = rows, c = cols, ld = a.ld;
             flatten(r, c, ld);
             const int vec = aligned16(a.x) && (r == 1 || (ld * eb) % 16 == 0);
-            const dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+            const dim3 g = stream_grid(r, c, 32, kAmaxGrid);
             np = (int)(g.x * g.y);
             hipLaunchKernelGGL(k_amax_partials<DT>, g, dim3(kThreads), 0, stream, a.x, r, c, ld, vec,
                                a.partials);
@@ -1759,7 +1759,7 @@ hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos
     int64_t r = rows, c = cols, l = a.ld;
     flatten(r, c, l);
     const int vec = aligned16(a.x) && (r == 1 || (l * eb) % 16 == 0);
-    dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+    dim3 g = stream_grid(r, c, 32, kAmaxGrid);
     if (rows == 0 || cols == 0) { r = 0; g = dim3(1, 1, 1); }
     if (a.dtype == FP8_IN_BF16)
         hipLaunchKernelGGL(k_amax_partials<0>, g, dim3(kThreads), 0, stream, a.x, r, c, l, vec, a.partials);
@@ -1790,7 +1790,7 @@ hipError_t launch_amax_partials(const void* x, int dtype, int64_t rows, int64_t 
     int64_t r = rows, c = cols, l = ld;
     flatten(r, c, l);
     const int vec = aligned16(x) && (r == 1 || (l * eb) % 16 == 0);
-    dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+    dim3 g = stream_grid(r, c, 32, kAmaxGrid);
     if (rows == 0 || cols == 0) { r = 0; g = dim3(1, 1, 1); }
     if (dtype == FP8_IN_BF16)
         hipLaunchKernelGGL(k_amax_partials<0>, g, dim3(kThreads), 0, stream, x, r, c, l, vec, partials);
@@ -1807,7 +1807,7 @@ hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t co
     int64_t r = rows, c = cols, l = ld;
     flatten(r, c, l);
     const int vec = aligned16(x) && (r == 1 || (l * eb) % 16 == 0);
-    dim3 g = stream_grid(r, c, 32, kAmaxPartials);
+    dim3 g = stream_grid(r, c, 32, kAmaxGrid);
     if (rows == 0 || cols == 0) { r = 0; g = dim3(1, 1, 1); }
     if (dtype == FP8_IN_BF16)
         hipLaunchKernelGGL(k_amax_partials<0>, g, dim3(kThreads), 0, stream, x, r, c, l, vec, partials);

@@ -129,3 +129,27 @@ def test_quantize_random_shapes(i, rows, cols):
         if want_t:
             assert np.array_equal(qt, oqt), f"{what}: transposed codes differ"
         assert same_counters(c, oc), f"{what}: counters gpu {c} oracle {oc}"
+
+
+@pytest.mark.parametrize("i,rows,cols", _quant_cases())
+def test_quantize_random_shapes_given_scales(i, rows, cols):
+    """Given scales (per tensor, per 1x128 tile, per 128x128 block) between a
+    third and three times amax / fmax, so that some elements saturate and
+    the rest take the corrected quotient below the scale's limit: bytes,
+    transposed bytes and counters bit-exact, ragged edges included."""
+    fmt = (fm.E4M3, fm.E5M2)[(i + 1) % 2]
+    fmax = 448.0 if fmt == fm.E4M3 else 57344.0
+    x = synth.channel_scaled_bf16(450 + i, 0, 5, (rows, cols))
+    amax = float(np.abs(synth.bf16_bits_to_f32(x)).max())
+    g = np.random.default_rng(460 + i)
+    xd = dev_bf16(x)
+    for gran, want_t in ((fm.TENSOR, False), (fm.TENSOR, True), (fm.ROW_1x128, False), (fm.BLOCK_128x128, True)):
+        shape = oracle.scale_shape(gran, rows, cols)
+        sc = (amax / fmax * g.uniform(1 / 3, 3, size=shape)).astype(np.float32)
+        q, qt, _, c = gpu_quantize(xd, fmt, gran, fm.GIVEN, sc, want_t)
+        oq, oqt, _, oc = oracle.quantize(x, fmt, gran, oracle.GIVEN, sc, want_t)
+        what = f"case {i}: {rows}x{cols} format {fmt} granularity {gran} transposed {want_t}, given scales"
+        assert np.array_equal(q, oq), f"{what}: {int((q != oq).sum())} codes differ"
+        if want_t:
+            assert np.array_equal(qt, oqt), f"{what}: transposed codes differ"
+        assert same_counters(c, oc), f"{what}: counters gpu {c} oracle {oc}"
