@@ -41,8 +41,10 @@ using gemm::v4f;
 using gemm::v4u;
 using gemm::v8i;
 
-constexpr int kAsN = 256;                    // output columns per unit (64 per wave)
-constexpr int kBF = 4;                       // B fragments per wave and K step
+// A unit is 64 BF output columns: each wave takes 16 BF of them as BF B
+// fragments per K step (BF = 4, 256 columns; short A: BF = 2, 128 columns).
+template <int BF>
+constexpr int unit_cols() { return 64 * BF; }
 constexpr int kAsKB = kAstatK / 128;         // 128-deep MFMA steps per unit
 constexpr int kAsChunks = kAstatK / 16;      // 16-byte chunks per panel row
 constexpr int kAsThreads = 256;
@@ -59,7 +61,8 @@ static_assert(kAstatK / 128 % kBRing == 0 && kBAhead < kBRing, "B ring");
 // as 16-17); the cast form ran 2% slower with them.  Short A (every unit of
 // 32-row panels fits in one round of workgroups) takes 32-row panels: one
 // unit per workgroup, whose time is then its B stream rather than the load
-// of a 156 KB panel.  A fragments are read from LDS `ahead` steps before
+// of a 156 KB panel; its units are 128 columns wide, so twice as many CUs
+// share the B stream.  A fragments are read from LDS `ahead` steps before
 // use, into a ring of `ring` slots (a unit's 6 x frags steps are a multiple
 // of it).
 constexpr int kAsRowsCodes = 208, kAsRowsCast = 192, kAsRowsShort = 32;
@@ -139,12 +142,14 @@ __device__ inline v8i a_frag(const AFragBase& ab, int i, int kb)
     return f;
 }
 
-// B fragment f (0..3) of K step kb for this wave: lane l (slot p = l % 16)
-// reads B row 64 w + 4 p + f of the unit, so lane p ends up holding output
-// columns 4 p .. 4 p + 3 of the wave's 64.  Rows past n read as zeros
-// (range check).  boff[f] is the lane's byte offset at K step 0; the K step
-// goes in soffset (every row in range stays in range with it: k <= ldb).
-__device__ inline v8i b_frag(__amdgpu_buffer_rsrc_t rs, const uint32_t (&boff)[kBF], int f, int kb)
+// B fragment f (0 .. BF - 1) of K step kb for this wave: lane l (slot
+// p = l % 16) reads B row 16 BF w + BF p + f of the unit, so lane p ends up
+// holding output columns BF p .. BF p + BF - 1 of the wave's 16 BF.  Rows
+// past n read as zeros (range check).  boff[f] is the lane's byte offset at
+// K step 0; the K step goes in soffset (every row in range stays in range
+// with it: k <= ldb).
+template <int BF>
+__device__ inline v8i b_frag(__amdgpu_buffer_rsrc_t rs, const uint32_t (&boff)[BF], int f, int kb)
 {
     const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)boff[f], 128 * kb, 0);
     const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)boff[f], 128 * kb + 16, 0);
@@ -154,11 +159,12 @@ __device__ inline v8i b_frag(__amdgpu_buffer_rsrc_t rs, const uint32_t (&boff)[k
     return v;
 }
 
+template <int BF>
 __device__ inline __amdgpu_buffer_rsrc_t b_rsrc(const AsArgs& p, int u, int u1)
 {
     const int nt = u < u1 ? u % p.ntn : 0;
-    const int n0 = nt * kAsN;
-    const int rows = u < u1 ? min(kAsN, p.n - n0) : 0;
+    const int n0 = nt * unit_cols<BF>();
+    const int rows = u < u1 ? min(unit_cols<BF>(), p.n - n0) : 0;
     return gemm::make_store_rsrc(const_cast<uint8_t*>(p.b) + (int64_t)n0 * p.ldb, (uint32_t)(rows * p.ldb));
 }
 
@@ -176,28 +182,35 @@ __device__ inline uint32_t block_reduce_key(uint32_t k)
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // Stores of rows 16 i .. 16 i + 15 (fragment i) of a finished unit: lane l
-// holds columns n0 + 64 w + 4 (l % 16) + 0..3 of rows 16 i + 4 (l / 16) + r
-// (one 8-byte store per row).  voff is the lane's byte offset (its columns
+// holds columns n0 + 16 BF w + BF (l % 16) + 0 .. BF - 1 of rows
+// 16 i + 4 (l / 16) + r (one 2 BF-byte store per row).  voff is the lane's
+// byte offset (its columns
 // and row group, or out of range), the row 16 i + r goes in soffset; a row
 // at or past `rows` (the rows of the panel inside the matrix) is dropped
 // through voff, so no store depends on whether the range check counts
 // soffset.  mx keeps the running maximum of the stored |bf16| patterns
 // (>= 0x7F80: an Inf or NaN was written; counted exactly at the end, see
 // recount()).
-template <int NF>
-__device__ inline void store_frag(const v4f (&acc)[NF][kBF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
+template <int NF, int BF>
+__device__ inline void store_frag(const v4f (&acc)[NF][BF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
                                   int rows, uint32_t row_bytes, float scale, us2& mx)
 {
+    static_assert(BF == 2 || BF == 4, "unit width");
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
     const int rq = 4 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
-        const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, lo & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, hi & 0x7FFF7FFFu));
         const uint32_t vo = 16 * i + rq + r < rows ? voff : gemm::kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, (int)((16 * i + r) * row_bytes), 2);   // nontemporal
+        const int so = (16 * i + r) * (int)row_bytes;
+        const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, lo & 0x7FFF7FFFu));
+        if constexpr (BF == 2) {
+            __builtin_amdgcn_raw_buffer_store_b32(lo, rc, (int)vo, so, 2);   // nontemporal
+        } else {
+            const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, hi & 0x7FFF7FFFu));
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, so, 2);   // nontemporal
+        }
     }
 }
 
@@ -349,7 +362,7 @@ __device__ __attribute__((always_inline)) inline void store_panel_t(const AsArgs
 
 // Exact count of the non-finite outputs this lane stored for units
 // u0 .. u1 - 1 (only run when one was seen: reads the outputs back).
-template <int ROWS>
+template <int ROWS, int BF>
 __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& p, int u0, int u1)
 {
     using P = Panel<ROWS>;
@@ -357,14 +370,14 @@ __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& 
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t n = 0;
     for (int u = u0; u < u1; ++u) {
-        const int m0 = (u / p.ntn) * P::rows, n0 = (u % p.ntn) * kAsN;
-        const int col = n0 + 64 * w + 4 * (l & 15);
+        const int m0 = (u / p.ntn) * P::rows, n0 = (u % p.ntn) * unit_cols<BF>();
+        const int col = n0 + 16 * BF * w + BF * (l & 15);
         if (col >= p.n) continue;
         for (int i = 0; i < P::frags; ++i)
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * i + 4 * (l >> 4) + r;
                 if (row >= p.m) continue;
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < BF; ++j)
                     n += (p.c[(int64_t)row * p.ldc + col + j] & 0x7F80u) == 0x7F80u;
             }
     }
@@ -382,7 +395,7 @@ __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& 
 // step's MFMAs (which write fragment 0); a fragment is overwritten by the
 // next unit only after it has been read out.  A scheduling barrier closes
 // every step (and separates its MFMAs from its read-out).
-template <int FA, int FB, int ASRC, int ROWS>
+template <int FA, int FB, int ASRC, int ROWS, int BF>
 __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
 {
     // unit range of this workgroup: ranges of one XCD (workgroups b = x mod 8)
@@ -415,15 +428,15 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     static_assert(ASRC == 0 || ROWS == kAsRowsCast, "panel of the cast form");
     using P = Panel<ROWS>;
     constexpr int kF = P::frags;
-    v4f acc[kF][kBF];
-    v8i bb[kBRing][kBF];
+    v4f acc[kF][BF];
+    v8i bb[kBRing][BF];
     v8i af[P::ring];
     const AFragBase ab = a_frag_base();
-    uint32_t boff[kBF];
+    uint32_t boff[BF];
 #pragma unroll
-    for (int f = 0; f < kBF; ++f) boff[f] = (uint32_t)((64 * w + 4 * (l & 15) + f) * p.ldb + 32 * (l >> 4));
+    for (int f = 0; f < BF; ++f) boff[f] = (uint32_t)((16 * BF * w + BF * (l & 15) + f) * p.ldb + 32 * (l >> 4));
     const uint32_t row_bytes = (uint32_t)(p.ldc * 2);
-    __amdgpu_buffer_rsrc_t rs_cur = b_rsrc(p, u0, u1), rs_next = b_rsrc(p, u0 + 1, u1);
+    __amdgpu_buffer_rsrc_t rs_cur = b_rsrc<BF>(p, u0, u1), rs_next = b_rsrc<BF>(p, u0 + 1, u1);
 
     int panel_loaded = -1;
     bool pending = false;   // fragment kF - 1 of the previous unit not stored yet
@@ -433,15 +446,15 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         return gemm::make_store_rsrc(p.c + (int64_t)m0 * p.ldc, (uint32_t)(min(P::rows, p.m - m0) * p.ldc * 2));
     };
     // the lane's store offset within a unit's rows: its columns and row group
-    // (n % 4 == 0: a column group is inside the matrix or past it entirely)
+    // (n % 4 == 0: a lane's BF columns are inside the matrix or past it entirely)
     auto col_off = [&](int n0) {
-        const int col = n0 + 64 * w + 4 * (l & 15);
+        const int col = n0 + 16 * BF * w + BF * (l & 15);
         return col < p.n ? (uint32_t)(col * 2) + (uint32_t)(4 * (l >> 4)) * row_bytes : gemm::kOutOfRange;
     };
 
     for (int u = u0; u < u1; ++u) {
         const int panel = u / p.ntn, nt = u - panel * p.ntn;
-        const int m0 = panel * P::rows, n0 = nt * kAsN;
+        const int m0 = panel * P::rows, n0 = nt * unit_cols<BF>();
         if (panel != panel_loaded) {
             if (pending) {
                 store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes,
@@ -462,7 +475,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
 #pragma unroll
             for (int kb = 0; kb < kBAhead; ++kb)
 #pragma unroll
-                for (int f = 0; f < kBF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
+                for (int f = 0; f < BF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
         }
         const __amdgpu_buffer_rsrc_t rc_prev = out_rsrc(pm0);
         const uint32_t co_prev = col_off(pn0);
@@ -477,7 +490,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
             if (i == 0) {
                 const int kf = kb + kBAhead;
 #pragma unroll
-                for (int f = 0; f < kBF; ++f)
+                for (int f = 0; f < BF; ++f)
                     bb[kf % kBRing][f] = kf < kAsKB ? b_frag(rs_cur, boff, f, kf) : b_frag(rs_next, boff, f, kf - kAsKB);
             }
             // A fragment of step s + 3 (wrapping to the next unit's first K step)
@@ -487,7 +500,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
             }
             const v8i& a = af[s % P::ring];
 #pragma unroll
-            for (int f = 0; f < kBF; ++f)
+            for (int f = 0; f < BF; ++f)
                 acc[i][f] = gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
             __builtin_amdgcn_sched_barrier(0);
             if (s == 0 && drain) store_frag(acc, kF - 1, rc_prev, co_prev, rows_prev, row_bytes, out_scale, mx);
@@ -498,11 +511,11 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         pm0 = m0;
         pn0 = n0;
         rs_cur = rs_next;
-        rs_next = b_rsrc(p, u + 2, u1);
+        rs_next = b_rsrc<BF>(p, u + 2, u1);
     }
     if (pending)
         store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
-    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ROWS>(p, u0, u1) : 0u;
+    const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ROWS, BF>(p, u0, u1) : 0u;
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
     if constexpr (ASRC == 1) flush_counters_block(p.ctr, sat, und, nan);
 }
@@ -513,7 +526,8 @@ bool astat_supported(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb, 
 {
     return k == kAstatK && m > 0 && n > 0 && n % 4 == 0 && ldc % 4 == 0 &&
            (reinterpret_cast<uintptr_t>(c) & 7u) == 0 && lda < ((int64_t)1 << 22) && ldb < ((int64_t)1 << 22) &&
-           ldc < ((int64_t)1 << 21) && (m + kAsMinRows - 1) / kAsMinRows * ((n + kAsN - 1) / kAsN) < ((int64_t)1 << 31);
+           ldc < ((int64_t)1 << 21) &&
+           (m + kAsMinRows - 1) / kAsMinRows * ((n + unit_cols<2>() - 1) / unit_cols<2>()) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream)
@@ -538,26 +552,29 @@ hipError_t launch_gemm_astat(const AstatArgs& g, int num_cus, hipStream_t stream
     p.c = static_cast<uint16_t*>(g.c);
     p.ldc = g.ldc;
     p.ctr = g.ctr;
+    // form: 0 codes (208-row panels, 256-column units), 1 cast from bf16
+    // (192 rows, 256 columns), 2 short A (32 rows, 128 columns)
+    int form = g.bf16_a ? 1 : 0;
+    if (!g.bf16_a && (g.m + kAsRowsShort - 1) / kAsRowsShort * ((g.n + unit_cols<2>() - 1) / unit_cols<2>()) <= num_cus)
+        form = 2;
+    const int rows = form == 1 ? kAsRowsCast : form == 2 ? kAsRowsShort : kAsRowsCodes;
+    const int cols = form == 2 ? unit_cols<2>() : unit_cols<4>();
     // n == 0 still walks one (empty) column unit per panel, so that the
     // panel's codes and counters are produced
-    p.ntn = std::max(1, (int)((g.n + kAsN - 1) / kAsN));
-    // panel form: 0 codes (208 rows), 1 cast from bf16 (192), 2 short A (32)
-    int form = g.bf16_a ? 1 : 0;
-    if (!g.bf16_a && (g.m + kAsRowsShort - 1) / kAsRowsShort * p.ntn <= num_cus) form = 2;
-    const int rows = form == 1 ? kAsRowsCast : form == 2 ? kAsRowsShort : kAsRowsCodes;
+    p.ntn = std::max(1, (int)((g.n + cols - 1) / cols));
     const int panels = (int)((g.m + rows - 1) / rows);
     p.units = panels * p.ntn;
     const int grid = std::min(p.units, num_cus);
     const int sel = (g.fa * 2 + g.fb) * 3 + form;
     switch (sel) {
-#define FP8MI_ASTAT(FA_, FB_, F_, S_, R_)                                                                \
-    case (FA_ * 2 + FB_) * 3 + F_:                                                                       \
-        hipLaunchKernelGGL((k_gemm_astat<FA_, FB_, S_, R_>), dim3(grid), dim3(kAsThreads), 0, stream, p); \
+#define FP8MI_ASTAT(FA_, FB_, F_, S_, R_, BF_)                                                                \
+    case (FA_ * 2 + FB_) * 3 + F_:                                                                            \
+        hipLaunchKernelGGL((k_gemm_astat<FA_, FB_, S_, R_, BF_>), dim3(grid), dim3(kAsThreads), 0, stream, p); \
         break;
 #define FP8MI_ASTAT3(FA_, FB_)                       \
-    FP8MI_ASTAT(FA_, FB_, 0, 0, kAsRowsCodes)        \
-    FP8MI_ASTAT(FA_, FB_, 1, 1, kAsRowsCast)         \
-    FP8MI_ASTAT(FA_, FB_, 2, 0, kAsRowsShort)
+    FP8MI_ASTAT(FA_, FB_, 0, 0, kAsRowsCodes, 4)     \
+    FP8MI_ASTAT(FA_, FB_, 1, 1, kAsRowsCast, 4)      \
+    FP8MI_ASTAT(FA_, FB_, 2, 0, kAsRowsShort, 2)
         FP8MI_ASTAT3(0, 0) FP8MI_ASTAT3(0, 1) FP8MI_ASTAT3(1, 0) FP8MI_ASTAT3(1, 1)
 #undef FP8MI_ASTAT3
 #undef FP8MI_ASTAT

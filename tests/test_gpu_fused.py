@@ -144,12 +144,13 @@ def test_fused_speedrun_forward_full():
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
 @pytest.mark.parametrize("m,n", [(1, 8), (191, 16), (193, 136), (207, 24), (208, 256), (209, 260), (417, 132),
-                                 (1000, 264), (2500, 1024), (300, 260), (64, 258), (500, 3072), (700, 3072)])
+                                 (1000, 264), (2500, 1024), (300, 260), (64, 258), (256, 3072), (500, 3072), (700, 3072)])
 def test_scaled_mm_k768_shapes(fa, fb, m, n):
     """fp8_scaled_mm with per-tensor scales and K = 768 (the A-stationary
     kernel): ragged panels and column units, every format pair.  Short A
-    (every unit of 32-row panels in one round: 500 x 3072 is 192 units)
-    takes 32-row panels, longer A 208-row ones (700 x 3072, 2500 x 1024)."""
+    (every unit of 32 rows x 128 columns in one round: 500 x 3072 is 384
+    units, 256 x 3072 192) takes that form, longer A 208-row panels and
+    256-column units (500 x 3072, 700 x 3072, 2500 x 1024)."""
     g = np.random.default_rng(m * 3 + n)
     a = synth.f32_to_bf16_bits((g.standard_normal((m, K))).astype(np.float32))
     aq, _, sa, _ = oracle.quantize(a, fa)
