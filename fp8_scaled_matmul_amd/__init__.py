@@ -36,7 +36,7 @@ EXPORTED = [
     "fp8_scaled_mm_workspace_size", "fp8_scaled_mm",
     "fp8_quantize_scaled_mm_workspace_size", "fp8_quantize_scaled_mm",
     "fp8_requant_workspace_size", "fp8_requant_weights",
-    "fp8_counters_reset",
+    "fp8_counters_reset", "fp8_debug_set_wait_limit",
 ]
 
 
@@ -105,6 +105,8 @@ def lib():
                                           ctypes.POINTER(ctypes.c_int), ctypes.c_int32, vp, sz, vp]
         L.fp8_counters_reset.restype = i32
         L.fp8_counters_reset.argtypes = [vp, vp]
+        L.fp8_debug_set_wait_limit.restype = ctypes.c_int32
+        L.fp8_debug_set_wait_limit.argtypes = [ctypes.c_int32]
         _lib = L
     return _lib
 

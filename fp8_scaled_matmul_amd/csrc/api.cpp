@@ -505,4 +505,6 @@ fp8_status fp8_counters_reset(fp8_counters* ctr, hipStream_t stream)
     return e == hipSuccess ? FP8_OK : hip_fail(e, "fp8_counters_reset launch");
 }
 
+int32_t fp8_debug_set_wait_limit(int32_t polls) { return fp8mi::set_once_wait_limit(polls); }
+
 }  // extern "C"

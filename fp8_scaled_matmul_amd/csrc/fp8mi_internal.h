@@ -76,6 +76,9 @@ hipError_t launch_amax_tensor(const void* x, int dtype, int64_t rows, int64_t co
 hipError_t launch_amax_grouped(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int gran, float* out, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// The bounded wait of the one-launch small-tensor quantize: polls before a
+// workgroup reads the whole tensor itself; returns the previous value.
+int set_once_wait_limit(int polls);
 hipError_t launch_quantize_delayed(const QuantArgs& a, float* hist, int32_t* pos, int len, hipStream_t stream);
 hipError_t launch_counters_reset(fp8_counters* ctr, hipStream_t stream);
 // Every cache's QuantArgs (FROM_AMAX; per-tensor ones with their partials).

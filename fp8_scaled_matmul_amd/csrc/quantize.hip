@@ -12,6 +12,7 @@
 // is two passes (amax partials, then cast) with the scale kept on the device;
 // fine-grained scaling is one fused pass per tile or block.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "device_common.h"
@@ -958,6 +959,63 @@ __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_e
 // tensors stay on that kernel: a form of this one that walked the tiles with
 // two workgroups per CU and the next tile prefetched was 3.5% slower on the
 // 65536 x 3072 gradient (fewer bytes in flight per CU).
+// The cast and stores of one tile held as w[4] by thread t of 512 (layout
+// above): codes row-major, and transposed through the LDS tile tl when qt is
+// not null.
+template <int FMT>
+__device__ __forceinline__ void tile128t_cast_store(const uint4 (&w)[4], float s, float r, bool fast, int64_t r0,
+                                                    int64_t c0, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                                    uint32_t* tl, uint32_t& sat, uint32_t& und, uint32_t& nan)
+{
+    const int t = threadIdx.x;
+    const int g = t >> 4, k = t & 15;
+    uint2 code[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        if (fast) {
+            code[i] = cast8_bf16_fast<FMT>(ws, s, r, und);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[2 * h] = bf16_lo(ws[h]);
+                v[2 * h + 1] = bf16_hi(ws[h]);
+            }
+            code[i] = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+        }
+        *reinterpret_cast<uint2*>(q + (r0 + 4 * g + i) * ldq + c0 + 8 * k) = code[i];
+    }
+    if (!qt) return;
+    // column cc = 8 k + 4 half + j of the tile: bytes of rows 4 g .. 4 g + 3,
+    // word g of LDS row cc, stored at word g ^ (4 ((cc / 8) % 8))
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t a = half ? code[0].y : code[0].x;
+        const uint32_t b = half ? code[1].y : code[1].x;
+        const uint32_t c = half ? code[2].y : code[2].x;
+        const uint32_t d = half ? code[3].y : code[3].x;
+        const uint32_t x0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+        const uint32_t x1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+        const uint32_t y0 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+        const uint32_t y1 = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+        const uint32_t col[4] = {__builtin_amdgcn_perm(y0, x0, 0x05040100u), __builtin_amdgcn_perm(y0, x0, 0x07060302u),
+                                 __builtin_amdgcn_perm(y1, x1, 0x05040100u), __builtin_amdgcn_perm(y1, x1, 0x07060302u)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tl[(8 * k + 4 * half + j) * 32 + (g ^ (4 * (k & 7)))] = col[j];
+    }
+    barrier_lds_only();
+    // output row c0 + cc (cc = t % 128), bytes r0 + 32 qq .. +31 (qq = t / 128):
+    // logical words 8 qq .. 8 qq + 7 of LDS row cc, two aligned groups of 4
+    const int cc = t & 127, qq = t >> 7;
+    const int sw = 4 * ((cc >> 3) & 7);
+    const uint4 lo = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq) ^ sw)]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq + 4) ^ sw)]);
+    uint8_t* dst = qt + (c0 + cc) * ldqt + r0 + 32 * qq;
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + 16) = hi;
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(8)))
     k_tile128t_bf16(const uint16_t* x, int64_t ld, int64_t tiles_c, float* scale, const uint32_t* partials, int np,
@@ -976,63 +1034,158 @@ __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_e
     } else {
         s = scale[0];
     }
-    const float r = 1.0f / s;
     uint32_t sat = 0, und = 0, nan = 0;
-
     const int64_t br = blockIdx.x / tiles_c;
     const int64_t r0 = br * kTile, c0 = (blockIdx.x - br * tiles_c) * kTile;
     uint4 w[4];
-    {
-        const uint16_t* src = x + (r0 + 4 * g) * ld + c0 + 8 * k;
+    const uint16_t* src = x + (r0 + 4 * g) * ld + c0 + 8 * k;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = ld_stream(src + i * ld);
+    for (int i = 0; i < 4; ++i) w[i] = ld_stream(src + i * ld);
+    tile128t_cast_store<FMT>(w, s, 1.0f / s, fast, r0, c0, q, ldq, qt, ldqt, tl, sat, und, nan);
+    flush_counters_block(ctr, sat, und, nan);
+}
+
+// ------------------------------------------------------------------ per-tensor quantize of a small tensor in one launch
+// A bf16 tensor of whole 128 x 128 tiles, at most one tile per CU (and at
+// most kOnceMaxTiles), per-tensor scale from its amax: one launch instead of
+// the amax pass and the cast.  Each 512-thread workgroup loads its tile,
+// reduces the tile's amax key, publishes it in the workspace and waits until
+// every tile's key is there, then merges them, derives the scale and casts
+// its tile from registers (codes, and the transposed copy when asked).
+//
+// The keys are matched to the call by a tag: every workgroup reads the
+// workspace's call counter before it publishes (so all read the same value
+// c: a workgroup only adds its departure to the counter after it has seen
+// every tile's key, which each workgroup publishes after its read), writes
+// its key and then, with release order, the tag c + 1, and waits (acquire)
+// for the tag c + 1 in every slot.  Each call advances the counter by its
+// tile count, so tags left by an earlier call on the same workspace never
+// match; a workspace that arrives with other contents matches only if a
+// 64-bit word happens to equal c + 1.  The wait is bounded: a workgroup that
+// has not seen every key after `spin_limit` polls (other workgroups not
+// resident, or a call on another stream sharing the workspace, which the
+// workspace contract excludes) reads the whole tensor for the amax itself:
+// slower, the same scale, and every workgroup finishes.
+constexpr int kOnceMaxTiles = 256;
+struct OnceSlot {
+    uint64_t tag;
+    uint32_t key;
+    uint32_t pad;
+};
+struct OnceSync {
+    uint64_t calls;
+    uint64_t pad[7];
+    OnceSlot slot[kOnceMaxTiles];
+};
+static_assert(sizeof(OnceSync) <= kAmaxWorkspaceBytes, "the amax workspace holds the call's slots");
+
+// The amax key of the whole tensor (rows x cols, whole tiles, 16-byte rows)
+// read by one workgroup: the fallback of a wait that did not complete.
+__device__ inline uint32_t tensor_key_one_workgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld)
+{
+    const int64_t vpr = cols / 8, nv = rows * vpr;
+    us2 m = us2{0, 0};
+    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+        const int64_t r = v / vpr;
+        m = pkmax8(m, *reinterpret_cast<const uint4*>(x + r * ld + (v - r * vpr) * 8));
     }
-    {
-        uint2 code[4];
+    uint32_t key = pk_raw(m);
+    if (block_key_merge(key) >= kRawNonFinite) {
+        key = 0;
+        for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+            const int64_t r = v / vpr;
+            const uint4 w = *reinterpret_cast<const uint4*>(x + r * ld + (v - r * vpr) * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                key = key_merge(key, absbits_bf16(ws[h] & 0xFFFFu));
+                key = key_merge(key, absbits_bf16(ws[h] >> 16));
+            }
+        }
+    }
+    return block_key_merge(key);
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(8)))
+    k_tile128t_once(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* scale, OnceSync* sync,
+                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, fp8_counters* ctr, int pow2, int spin_limit)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t tl[kTile * kTile / 4];
+    __shared__ uint32_t s_key;
+    const int t = threadIdx.x;
+    const int g = t >> 4, k = t & 15;
+    const int64_t tiles_c = cols / kTile;
+    const int ntiles = (int)gridDim.x;
+    const int64_t br = blockIdx.x / tiles_c;
+    const int64_t r0 = br * kTile, c0 = (blockIdx.x - br * tiles_c) * kTile;
+    uint4 w[4];
+    const uint16_t* src = x + (r0 + 4 * g) * ld + c0 + 8 * k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = ld_stream(src + i * ld);
+
+    // this tile's key (the exact merge only for a tile holding Inf or NaN)
+    us2 m = us2{0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = pkmax8(m, w[i]);
+    uint32_t key = block_key_merge(pk_raw(m));
+    if (key >= kRawNonFinite) {
+        uint32_t e = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-            if (fast) {
-                code[i] = cast8_bf16_fast<FMT>(ws, s, r, und);
-            } else {
-                float v[8];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    v[2 * h] = bf16_lo(ws[h]);
-                    v[2 * h + 1] = bf16_hi(ws[h]);
-                }
-                code[i] = cast8<FMT, false>(v, s, 0.0f, sat, und, nan);
+            for (int h = 0; h < 4; ++h) {
+                e = key_merge(e, absbits_bf16(ws[h] & 0xFFFFu));
+                e = key_merge(e, absbits_bf16(ws[h] >> 16));
             }
-            *reinterpret_cast<uint2*>(q + (r0 + 4 * g + i) * ldq + c0 + 8 * k) = code[i];
         }
-        // column cc = 8 k + 4 half + j of the tile: bytes of rows 4 g .. 4 g + 3,
-        // word g of LDS row cc, stored at word g ^ (4 ((cc / 8) % 8))
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint32_t a = half ? code[0].y : code[0].x;
-            const uint32_t b = half ? code[1].y : code[1].x;
-            const uint32_t c = half ? code[2].y : code[2].x;
-            const uint32_t d = half ? code[3].y : code[3].x;
-            const uint32_t x0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-            const uint32_t x1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-            const uint32_t y0 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
-            const uint32_t y1 = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
-            const uint32_t col[4] = {__builtin_amdgcn_perm(y0, x0, 0x05040100u), __builtin_amdgcn_perm(y0, x0, 0x07060302u),
-                                     __builtin_amdgcn_perm(y1, x1, 0x05040100u), __builtin_amdgcn_perm(y1, x1, 0x07060302u)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) tl[(8 * k + 4 * half + j) * 32 + (g ^ (4 * (k & 7)))] = col[j];
-        }
-        barrier_lds_only();
-        // output row c0 + cc (cc = t % 128), bytes r0 + 32 qq .. +31 (qq = t / 128):
-        // logical words 8 qq .. 8 qq + 7 of LDS row cc, two aligned groups of 4
-        const int cc = t & 127, qq = t >> 7;
-        const int sw = 4 * ((cc >> 3) & 7);
-        const uint4 lo = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq) ^ sw)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&tl[cc * 32 + ((8 * qq + 4) ^ sw)]);
-        uint8_t* dst = qt + (c0 + cc) * ldqt + r0 + 32 * qq;
-        *reinterpret_cast<uint4*>(dst) = lo;
-        *reinterpret_cast<uint4*>(dst + 16) = hi;
+        key = block_key_merge(e);
     }
+
+    // publish, wait for every tile's key, merge (wave 0)
+    __shared__ int s_complete;
+    if (t < 64) {
+        uint64_t c = 0;
+        if (t == 0) {
+            c = __hip_atomic_load(&sync->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync->slot[blockIdx.x].key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync->slot[blockIdx.x].tag, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint64_t want = __shfl(c, 0) + 1;
+        bool seen = false;
+        for (int it = 0; it < spin_limit; ++it) {
+            bool mine = true;
+            for (int j = t; j < ntiles; j += 64)
+                mine &= __hip_atomic_load(&sync->slot[j].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+            if (__all(mine)) {
+                seen = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        uint32_t kk = 0;
+        if (seen) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the keys after their tags
+            for (int j = t; j < ntiles; j += 64)
+                kk = key_merge(kk, __hip_atomic_load(&sync->slot[j].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            kk = wave_key_merge(kk);
+        }
+        if (t == 0) {
+            s_key = kk;
+            s_complete = seen;
+            __hip_atomic_fetch_add(&sync->calls, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    // the wait did not complete: this workgroup reads the whole tensor
+    const uint32_t kk = s_complete ? s_key : tensor_key_one_workgroup(x, rows, cols, ld);
+
+    const float s = scale_rule<FMT>(key_amax(kk), pow2);
+    const bool fast = !key_special(kk) && s >= kCorrectedQuotMinScale;
+    if (blockIdx.x == 0 && t == 0) scale[0] = s;
+    uint32_t sat = 0, und = 0, nan = 0;
+    tile128t_cast_store<FMT>(w, s, 1.0f / s, fast, r0, c0, q, ldq, qt, ldqt, tl, sat, und, nan);
     flush_counters_block(ctr, sat, und, nan);
 }
 
@@ -1536,6 +1689,24 @@ hipError_t launch_tiles(const QuantArgs& a, int vec, const uint32_t* parts, int 
     return hipGetLastError();
 }
 
+// Polls of k_tile128t_once's bounded wait before a workgroup falls back to
+// reading the whole tensor (0: always fall back).
+std::atomic<int> g_once_wait_limit{1 << 14};
+
+// A per-tensor quantize from amax that k_tile128t_once takes in one launch:
+// bf16, whole 128 x 128 tiles, at most one tile per CU, the layouts of its
+// vector loads and stores, and an 8-byte aligned workspace for the call's
+// slots.
+bool once_fits(const QuantArgs& a)
+{
+    const int64_t nt = (a.rows / kTile) * (a.cols / kTile);
+    return a.dtype == FP8_IN_BF16 && a.rows > 0 && a.rows % kTile == 0 && a.cols % kTile == 0 &&
+           nt <= std::min<int64_t>(kOnceMaxTiles, num_cus()) && aligned16(a.x) && (a.ld * 2) % 16 == 0 &&
+           (reinterpret_cast<uintptr_t>(a.q) & 7u) == 0 && a.ldq % 8 == 0 &&
+           (!a.qt || (aligned16(a.qt) && a.ldqt % 16 == 0)) && a.partials &&
+           (reinterpret_cast<uintptr_t>(a.partials) & 7u) == 0;
+}
+
 template <int FMT, int DT>
 hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
 {
@@ -1543,6 +1714,14 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t stream)
     const int64_t rows = a.rows, cols = a.cols;
     if (a.gran == FP8_TENSOR) {
         const bool from_amax = a.mode == FP8_SCALE_FROM_AMAX;
+        if (DT == 0 && from_amax && once_fits(a)) {
+            const unsigned nt = (unsigned)((rows / kTile) * (cols / kTile));
+            hipLaunchKernelGGL((k_tile128t_once<FMT>), dim3(nt), dim3(kBlkThreads), 0, stream,
+                               static_cast<const uint16_t*>(a.x), rows, cols, a.ld, a.scale,
+                               reinterpret_cast<OnceSync*>(a.partials), a.q, a.ldq, a.qt, a.ldqt, a.ctr, a.pow2,
+                               g_once_wait_limit.load(std::memory_order_relaxed));
+            return hipGetLastError();
+        }
         int np = 0;
         if (from_amax) {
             int64_t r = rows, c = cols, ld = a.ld;
@@ -1635,6 +1814,8 @@ hipError_t noalloc_scratch(uint32_t** out)
 }
 
 // ------------------------------------------------------------------ launchers
+int set_once_wait_limit(int polls) { return g_once_wait_limit.exchange(polls < 0 ? 0 : polls); }
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)
 {
     if (a.rows == 0 || a.cols == 0) {

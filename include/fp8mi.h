@@ -136,7 +136,12 @@ fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, 
  *          this write and a GEMM that reads q_t as an operand.
  *   ctr    optional counters (NULL = none).
  *   workspace  TENSOR + FROM_AMAX needs fp8_quantize_workspace_size() bytes;
- *          the other modes need none.
+ *          the other modes need none.  Its contents on entry do not matter,
+ *          and it must not be in use by another call at the same time.  A
+ *          small per-tensor call (bf16, whole 128x128 tiles, at most 256
+ *          tiles and one per CU, 8-byte aligned workspace) runs as one
+ *          launch whose workgroups exchange their tile maxima through the
+ *          workspace, matched to the call by a counter kept there.
  * Alignment: x, q, q_t any; fast vector paths are taken when rows start on
  * 16-byte boundaries. */
 size_t     fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity gran,
@@ -311,6 +316,14 @@ fp8_status fp8_requant_weights(const fp8_weight_cache* caches, const void* const
 
 /* Zero a counter block on `stream` (a small fill kernel, safe to capture). */
 fp8_status fp8_counters_reset(fp8_counters* ctr, hipStream_t stream);
+
+/* Testing aid for the one-launch path of small per-tensor quantize calls
+ * (see fp8_quantize's workspace).  Each workgroup waits, a bounded number of
+ * polls, for every tile's maximum; one whose wait runs out reads the whole
+ * tensor itself (the same scale and codes, slower).  Sets that bound for
+ * the calls that follow, from any thread (0: every workgroup reads the
+ * whole tensor), and returns the previous one; the default is 16384. */
+int32_t fp8_debug_set_wait_limit(int32_t polls);
 
 #ifdef __cplusplus
 }

@@ -298,3 +298,51 @@ def test_caller_workspace():
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
     with pytest.raises(ValueError, match="workspace needs"):
         fm.quantize(xd, fm.E4M3, workspace=ws[: wsb - 1])
+
+
+ONE_LAUNCH_SHAPES = [(128, 128), (256, 768), (3072, 768), (128, 32768), (2048, 2048)]
+
+
+def _one_launch_cases(fmt, mode, ws, what):
+    """Per-tensor quantize of tensors the one-launch kernel takes (bf16,
+    whole 128x128 tiles, at most 256 tiles and one per CU), with and without
+    the transposed copy, on the caller's workspace ws, against the oracle."""
+    for i, shape in enumerate(ONE_LAUNCH_SHAPES):
+        x = synth.with_outliers_bf16(30 + i, shape, frac=0.01).copy()
+        if i == 2:
+            x[5, 7] = 0x7FC0      # NaN: the scale ignores it, the code is 0x7F | sign
+            x[100, 1] = 0xFF80    # -Inf: saturates
+        xd = dev_bf16(x)
+        for want_t in (False, True):
+            ctr = fm.Counters()
+            q, qt, s = fm.quantize(xd, fmt, fm.TENSOR, mode, want_t=want_t, counters=ctr, workspace=ws)
+            torch.cuda.synchronize()
+            if mode == fm.FROM_AMAX_POW2:
+                oq, oqt, os_, oc = oracle.quantize_pow2(x, fmt, oracle.TENSOR, want_t=want_t)
+            else:
+                oq, oqt, os_, oc = oracle.quantize(x, fmt, want_t=want_t)
+            w = f"{what} {shape} fmt {fmt} mode {mode} transposed {want_t}"
+            assert np.array_equal(host(s).reshape(-1), os_.reshape(-1)), f"{w}: scale"
+            assert np.array_equal(host(q), oq), f"{w}: codes"
+            if want_t:
+                assert np.array_equal(host(qt), oqt), f"{w}: transposed codes"
+            assert same_counters(ctr.read(), oc), f"{w}: counters"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_launch_small_tensors(fmt):
+    """Small per-tensor calls run as one launch whose workgroups exchange
+    their tile maxima through the workspace.  The workspace arrives holding
+    arbitrary bytes (random, then each call's own leftovers, with calls of
+    different tile counts in turn), and with the wait bound set to zero every
+    workgroup reads the whole tensor itself: bit-exact either way."""
+    wsb = fm.lib().fp8_quantize_workspace_size(128, 128, fm.TENSOR, fm.FROM_AMAX)
+    ws = torch.from_numpy(np.random.default_rng(9).integers(0, 256, wsb, dtype=np.uint8)).cuda()
+    _one_launch_cases(fmt, fm.FROM_AMAX, ws, "one launch")
+    _one_launch_cases(fmt, fm.FROM_AMAX_POW2, ws, "one launch, power-of-two")
+    prev = fm.lib().fp8_debug_set_wait_limit(0)
+    try:
+        _one_launch_cases(fmt, fm.FROM_AMAX, ws, "every workgroup reads the tensor")
+    finally:
+        fm.lib().fp8_debug_set_wait_limit(prev)
+    assert fm.lib().fp8_debug_set_wait_limit(prev) == prev
