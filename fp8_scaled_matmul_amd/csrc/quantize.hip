@@ -1106,8 +1106,9 @@ __device__ inline uint32_t tensor_key_one_workgroup(const uint16_t* x, int64_t r
     return block_key_merge(key);
 }
 
+// At most one workgroup per CU: its 8 waves may take 256 registers each.
 template <int FMT>
-__global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(2)))
     k_tile128t_once(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* scale, OnceSync* sync,
                     uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, fp8_counters* ctr, int pow2, int spin_limit)
 {
