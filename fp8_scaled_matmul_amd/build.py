@@ -31,8 +31,8 @@ FLAGS = [
 # Per-file extras.  The block-scaled GEMM promotes each MFMA result on the
 # VALU: MFMA results written straight to VGPRs save a copy out of AGPRs.
 EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         # the A-stationary kernel's 72-step unit loop must unroll fully (its
-         # register rings are indexed by the step)
+         # the A-stationary kernel's unit loop must unroll fully (its register
+         # rings are indexed by the step)
          "gemm_astat.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
 
 
