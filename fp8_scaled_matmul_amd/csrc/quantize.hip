@@ -1057,16 +1057,26 @@ __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_e
 // workspace's call counter before it publishes (so all read the same value
 // c: a workgroup only adds its departure to the counter after it has seen
 // every tile's key, which each workgroup publishes after its read), writes
-// its key and then, with release order, the tag c + 1, and waits (acquire)
-// for the tag c + 1 in every slot.  Each call advances the counter by its
-// tile count, so tags left by an earlier call on the same workspace never
-// match; a workspace that arrives with other contents matches only if a
-// 64-bit word happens to equal c + 1.  The wait is bounded: a workgroup that
+// its key and then, with release order, the tag T(c), and waits (acquire)
+// for T(c) in every slot.  T is a bijective 64-bit mix, so tags left by an
+// earlier call on the same workspace (each call advances the counter by its
+// tile count) never match, and words left by other uses of the workspace
+// (the amax pass's keys, whose neighbours can differ by one) match only by
+// a 64-bit coincidence.  The wait is bounded: a workgroup that
 // has not seen every key after `spin_limit` polls (other workgroups not
 // resident, or a call on another stream sharing the workspace, which the
 // workspace contract excludes) reads the whole tensor for the amax itself:
 // slower, the same scale, and every workgroup finishes.
 constexpr int kOnceMaxTiles = 256;
+// T(c): the finalizer of SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast
+// splittable pseudorandom number generators", OOPSLA 2014), a bijection.
+__device__ inline uint64_t once_tag(uint64_t c)
+{
+    uint64_t z = c + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
 struct OnceSlot {
     uint64_t tag;
     uint32_t key;
@@ -1151,9 +1161,9 @@ __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_e
         if (t == 0) {
             c = __hip_atomic_load(&sync->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&sync->slot[blockIdx.x].key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sync->slot[blockIdx.x].tag, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync->slot[blockIdx.x].tag, once_tag(c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
-        const uint64_t want = __shfl(c, 0) + 1;
+        const uint64_t want = once_tag(__shfl(c, 0));
         bool seen = false;
         for (int it = 0; it < spin_limit; ++it) {
             bool mine = true;

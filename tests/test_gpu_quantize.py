@@ -335,10 +335,18 @@ def test_one_launch_small_tensors(fmt):
     their tile maxima through the workspace.  The workspace arrives holding
     arbitrary bytes (random, then each call's own leftovers, with calls of
     different tile counts in turn), and with the wait bound set to zero every
-    workgroup reads the whole tensor itself: bit-exact either way."""
+    workgroup reads the whole tensor itself: bit-exact either way.  Between
+    rounds a large tensor's two-launch quantize writes its amax keys over the
+    same workspace."""
     wsb = fm.lib().fp8_quantize_workspace_size(128, 128, fm.TENSOR, fm.FROM_AMAX)
     ws = torch.from_numpy(np.random.default_rng(9).integers(0, 256, wsb, dtype=np.uint8)).cuda()
     _one_launch_cases(fmt, fm.FROM_AMAX, ws, "one launch")
+    # a large tensor's amax pass writes its partial keys over the same workspace
+    big = synth.with_outliers_bf16(40, (4096, 4096))
+    q, _, s = fm.quantize(dev_bf16(big), fmt, workspace=ws)
+    oq, _, os_, _ = oracle.quantize(big, fmt)
+    assert np.array_equal(host(q), oq) and np.array_equal(host(s).reshape(-1), os_.reshape(-1))
+    _one_launch_cases(fmt, fm.FROM_AMAX, ws, "one launch after a two-launch call")
     _one_launch_cases(fmt, fm.FROM_AMAX_POW2, ws, "one launch, power-of-two")
     prev = fm.lib().fp8_debug_set_wait_limit(0)
     try:
