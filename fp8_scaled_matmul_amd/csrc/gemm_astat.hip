@@ -79,6 +79,11 @@ struct Panel {
 };
 constexpr int kAsMinRows = kAsRowsShort, kAsMaxBytes = Panel<kAsRowsCodes>::bytes;
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding, with no LDS or export wait.
+constexpr unsigned waitcnt_vm(int n) { return (((unsigned)n >> 4) & 3u) << 14 | ((unsigned)n & 15u) | 7u << 4 | 15u << 8; }
+static_assert(waitcnt_vm(63) == 0xCF7Fu && waitcnt_vm(0) == 0x0F70u, "s_waitcnt encoding");
+
 struct AsArgs {
     const void* a;          // FP8 codes [m, k] (lda bytes) or bf16 [m, k] (lda elements)
     int64_t lda;
@@ -248,7 +253,7 @@ __device__ __attribute__((always_inline)) inline void load_panel(const AsArgs& p
             gemm::dma16(__builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)slot), (uint32_t)(r * p.lda + 16 * lc),
                         ra);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // a wait the compiler sees: the B ring is complete too
     } else {
         const __amdgpu_buffer_rsrc_t rx = gemm::make_store_rsrc(
             const_cast<uint16_t*>(static_cast<const uint16_t*>(p.a)) + (int64_t)m0 * p.lda,
@@ -437,8 +442,16 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
     for (int f = 0; f < BF; ++f) boff[f] = (uint32_t)((16 * BF * w + BF * (l & 15) + f) * p.ldb + 32 * (l >> 4));
     const uint32_t row_bytes = (uint32_t)(p.ldc * 2);
     __amdgpu_buffer_rsrc_t rs_cur = b_rsrc<BF>(p, u0, u1), rs_next = b_rsrc<BF>(p, u0 + 1, u1);
+    // Codes in A: the B ring is loaded once here and then only by the unit
+    // body (the next unit's first steps), live across panel loads, so every
+    // unit starts from the same registers.
+    if constexpr (ASRC == 0) {
+#pragma unroll
+        for (int kb = 0; kb < kBAhead; ++kb)
+#pragma unroll
+            for (int f = 0; f < BF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
+    }
 
-    int panel_loaded = -1;
     bool pending = false;   // fragment kF - 1 of the previous unit not stored yet
     int pm0 = 0, pn0 = 0;
 
@@ -452,66 +465,73 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         return col < p.n ? (uint32_t)(col * 2) + (uint32_t)(4 * (l >> 4)) * row_bytes : gemm::kOutOfRange;
     };
 
-    for (int u = u0; u < u1; ++u) {
-        const int panel = u / p.ntn, nt = u - panel * p.ntn;
-        const int m0 = panel * P::rows, n0 = nt * unit_cols<BF>();
-        if (panel != panel_loaded) {
-            if (pending) {
-                store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes,
-                           out_scale, mx);
-                pending = false;
-            }
-            __syncthreads();   // every wave is done with the previous panel
-            const bool own = ASRC == 1 && nt == 0;
-            load_panel<FA, ASRC, ROWS>(p, m0, own, sa, rcp, fast, sat, und, nan);
-            __syncthreads();
-            if (ASRC == 1 && own && p.xqt) store_panel_t(p, m0);
-            panel_loaded = panel;
-            // the first A fragments of the panel (the same for every unit of
-            // it), and this unit's first B steps again: the B ring is left
-            // dead across the panel load, whose loads then have its registers
+    // Outer loop: the panels of the unit range; inner loop: the units of one
+    // panel, a body with no branch around it.  (With the panel load as a
+    // branch inside one unit loop, the compiler joined the two paths at every
+    // unit start and made the first MFMAs wait for every outstanding memory
+    // operation, the previous unit's output stores included.)
+    for (int u = u0; u < u1;) {
+        const int panel = u / p.ntn;
+        const int m0 = panel * P::rows;
+        const int u_end = min(u1, (panel + 1) * p.ntn);
+        if (pending) {
+            store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
+            pending = false;
+        }
+        __syncthreads();   // every wave is done with the previous panel
+        const bool own = ASRC == 1 && u == panel * p.ntn;
+        load_panel<FA, ASRC, ROWS>(p, m0, own, sa, rcp, fast, sat, und, nan);
+        __syncthreads();
+        if (ASRC == 1 && own && p.xqt) store_panel_t(p, m0);
+        // the first A fragments of the panel (the same for every unit of it);
+        // bf16 A: this unit's first B steps again (the B ring is left dead
+        // across the cast, whose loads then have its registers)
 #pragma unroll
-            for (int j = 0; j < P::ahead; ++j) af[j] = a_frag(ab, j % kF, j / kF);
+        for (int j = 0; j < P::ahead; ++j) af[j] = a_frag(ab, j % kF, j / kF);
+        if constexpr (ASRC == 1) {
 #pragma unroll
             for (int kb = 0; kb < kBAhead; ++kb)
 #pragma unroll
                 for (int f = 0; f < BF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
         }
-        const __amdgpu_buffer_rsrc_t rc_prev = out_rsrc(pm0);
-        const uint32_t co_prev = col_off(pn0);
-        const int rows_prev = min(P::rows, p.m - pm0);
         const __amdgpu_buffer_rsrc_t rc = out_rsrc(m0);
-        const uint32_t co = col_off(n0);
         const int rows = min(P::rows, p.m - m0);
-        const bool drain = pending;
+        for (; u < u_end; ++u) {
+            const int n0 = (u - panel * p.ntn) * unit_cols<BF>();
+            const uint32_t co = col_off(n0);
+            const uint32_t co_prev = col_off(pn0);   // the previous unit of the same panel
+            const bool drain = pending;
 #pragma unroll
-        for (int s = 0; s < kAsKB * kF; ++s) {
-            const int kb = s / kF, i = s % kF;
-            if (i == 0) {
-                const int kf = kb + kBAhead;
+            for (int s = 0; s < kAsKB * kF; ++s) {
+                const int kb = s / kF, i = s % kF;
+                if (i == 0) {
+                    const int kf = kb + kBAhead;
+#pragma unroll
+                    for (int f = 0; f < BF; ++f)
+                        bb[kf % kBRing][f] =
+                            kf < kAsKB ? b_frag(rs_cur, boff, f, kf) : b_frag(rs_next, boff, f, kf - kAsKB);
+                }
+                // A fragment of step s + 3 (wrapping to the next unit's first K step)
+                {
+                    const int s3 = (s + P::ahead) % (kAsKB * kF);
+                    af[(s + P::ahead) % P::ring] = a_frag(ab, s3 % kF, s3 / kF);
+                }
+                const v8i& a = af[s % P::ring];
 #pragma unroll
                 for (int f = 0; f < BF; ++f)
-                    bb[kf % kBRing][f] = kf < kAsKB ? b_frag(rs_cur, boff, f, kf) : b_frag(rs_next, boff, f, kf - kAsKB);
+                    acc[i][f] =
+                        gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s == 0 && drain) store_frag(acc, kF - 1, rc, co_prev, rows, row_bytes, out_scale, mx);
+                if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, rows, row_bytes, out_scale, mx);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // A fragment of step s + 3 (wrapping to the next unit's first K step)
-            {
-                const int s3 = (s + P::ahead) % (kAsKB * kF);
-                af[(s + P::ahead) % P::ring] = a_frag(ab, s3 % kF, s3 / kF);
-            }
-            const v8i& a = af[s % P::ring];
-#pragma unroll
-            for (int f = 0; f < BF; ++f)
-                acc[i][f] = gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (s == 0 && drain) store_frag(acc, kF - 1, rc_prev, co_prev, rows_prev, row_bytes, out_scale, mx);
-            if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, rows, row_bytes, out_scale, mx);
-            __builtin_amdgcn_sched_barrier(0);
+            pending = true;
+            pm0 = m0;
+            pn0 = n0;
+            rs_cur = rs_next;
+            rs_next = b_rsrc<BF>(p, u + 2, u1);
         }
-        pending = true;
-        pm0 = m0;
-        pn0 = n0;
-        rs_cur = rs_next;
-        rs_next = b_rsrc<BF>(p, u + 2, u1);
     }
     if (pending)
         store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
