@@ -290,16 +290,23 @@ class Counters:
         return {f: int(v) & 0xFFFFFFFFFFFFFFFF for f, v in zip(self.FIELDS, vals)}
 
 
-def amax(x, gran: int = TENSOR):
+def amax(x, gran: int = TENSOR, workspace=None):
+    """workspace: optional uint8 device tensor of at least
+    fp8_amax_workspace_size(rows, cols, gran) bytes (allocated per call when
+    None)."""
     torch = _torch()
     _check_tensor(x, "x", (torch.bfloat16, torch.float32), unit_col_stride=True)
-    _check_devices(x)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", (torch.uint8,), contiguous=True)
+    _check_devices(x, workspace)
     rows, cols = x.shape
     out = torch.empty(scale_shape(gran, rows, cols), dtype=torch.float32, device=x.device)
     wsb = lib().fp8_amax_workspace_size(rows, cols, gran)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    if workspace is not None and workspace.numel() < wsb:
+        raise ValueError(f"workspace needs {wsb} bytes, got {workspace.numel()}")
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
     check(fp8_amax(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), gran, out.data_ptr(),
-                   ws.data_ptr(), wsb, _stream()))
+                   ws.data_ptr(), ws.numel(), _stream()))
     return out
 
 

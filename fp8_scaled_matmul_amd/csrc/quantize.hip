@@ -144,6 +144,9 @@ __device__ inline uint32_t block_key_merge(uint32_t k)
 // ------------------------------------------------------------------ amax
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// s_waitcnt vmcnt(0) (gfx9 encoding, no LDS or export wait) as a builtin.
+constexpr unsigned kWaitVmcnt0 = 0x0F70u;
+
 // 16 bytes read once: a nontemporal load (the data is not reused).
 __device__ inline uint4 ld_stream(const void* p)
 {
@@ -1077,6 +1080,23 @@ __device__ inline uint64_t once_tag(uint64_t c)
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     return z ^ (z >> 31);
 }
+// Publish a key, then its tag, for a reader elsewhere on the chip that reads
+// the tag and then the key with agent-scope atomic loads.  Both stores are
+// agent-scope atomics, which the memory system keeps coherent at that scope
+// once they complete; waiting for the key's store to complete before the
+// tag's store is issued orders them.  (A release store of the tag would
+// also write back this XCD's L2 for the sake of ordinary stores, of which
+// there are none to publish: with hundreds of workgroups publishing at
+// once those write-backs cost several microseconds.)
+__device__ inline void publish_key(uint32_t* key_slot, uint32_t key, uint64_t* tag_slot, uint64_t tag)
+{
+    __hip_atomic_store(key_slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // no compiler reordering across
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __hip_atomic_store(tag_slot, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct OnceSlot {
     uint64_t tag;
     uint32_t key;
@@ -1160,8 +1180,7 @@ __global__ void __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_e
         uint64_t c = 0;
         if (t == 0) {
             c = __hip_atomic_load(&sync->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sync->slot[blockIdx.x].key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sync->slot[blockIdx.x].tag, once_tag(c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            publish_key(&sync->slot[blockIdx.x].key, key, &sync->slot[blockIdx.x].tag, once_tag(c));
         }
         const uint64_t want = once_tag(__shfl(c, 0));
         bool seen = false;

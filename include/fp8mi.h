@@ -96,7 +96,9 @@ const char* fp8_last_error(void);
  *          [ceil(rows/128), ceil(cols/128)] (BLOCK_128x128), row-major.
  *          A group with no finite element gets 0.
  *   workspace  TENSOR needs fp8_amax_workspace_size() bytes (partial maxima);
- *          other granularities need none (may be NULL).
+ *          other granularities need none (may be NULL).  Its contents on
+ *          entry do not matter, and it must not be in use by another call at
+ *          the same time.
  * Sizes of zero are allowed (TENSOR writes 0). */
 size_t     fp8_amax_workspace_size(int64_t rows, int64_t cols, fp8_granularity gran);
 fp8_status fp8_amax(const void* x, fp8_dtype dtype, int64_t rows, int64_t cols, int64_t ld,

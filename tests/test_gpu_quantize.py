@@ -207,6 +207,57 @@ def test_amax_entry_point(fmt):
         assert np.array_equal(got.reshape(-1), oracle.amax(x, gran).reshape(-1)), gran
 
 
+def _amax_cases():
+    """(host array, device tensor, what) for the per-tensor amax: bf16 and
+    fp32, contiguous (one long row), strided rows (ld > cols), rows that are
+    not 16-byte aligned, Inf and NaN present, all NaN, one element, and a
+    tensor that takes the full 512 workgroups."""
+    g = np.random.default_rng(21)
+    out = []
+    a = synth.with_outliers_bf16(22, (300, 700), frac=0.01)
+    out.append((a, dev_bf16(a), "bf16 300x700"))
+    b = synth.with_outliers_bf16(23, (2048, 4096), frac=0.001)
+    out.append((b, dev_bf16(b), "bf16 2048x4096"))
+    f = g.normal(size=(513, 1000)).astype(np.float32)
+    f[7, 9], f[300, 2] = np.inf, np.nan
+    out.append((f, dev_f32(f), "fp32 513x1000 with Inf and NaN"))
+    wide = synth.with_outliers_bf16(24, (257, 1024), frac=0.01)
+    out.append((np.ascontiguousarray(wide[:, :1000]), dev_bf16(wide)[:, :1000], "bf16 257x1000, ld 1024"))
+    odd = synth.with_outliers_bf16(25, (129, 333), frac=0.01)
+    out.append((np.ascontiguousarray(odd[:, :331]), dev_bf16(odd)[:, :331], "bf16 129x331, ld 333"))
+    nan = np.full((3, 64), 0x7FC0, dtype=np.uint16)
+    out.append((nan, dev_bf16(nan), "bf16 all NaN"))
+    one = np.array([[0xC2F7]], dtype=np.uint16)
+    out.append((one, dev_bf16(one), "bf16 one element"))
+    return out
+
+
+def test_amax_layouts_and_caller_workspace():
+    """The per-tensor amax on the cases above, through a workspace the caller
+    holds: random bytes at first, then each call's leftovers, then the keys
+    of a large tensor's quantize; and one that is not 8-byte aligned.
+    Bit-exact every time."""
+    cases = _amax_cases()
+    wsb = fm.lib().fp8_amax_workspace_size(1, 1, fm.TENSOR)
+    raw = torch.from_numpy(np.random.default_rng(26).integers(0, 256, wsb + 8, dtype=np.uint8)).cuda()
+
+    def run(ws, what):
+        for x, xd, name in cases:
+            got = host(fm.amax(xd, fm.TENSOR, workspace=ws)).reshape(-1)
+            assert np.array_equal(got, oracle.amax(x, fm.TENSOR).reshape(-1)), f"{what}: {name}"
+
+    ws = raw[:wsb]
+    run(ws, "random workspace")
+    run(ws, "the previous calls' leftovers")
+    big = synth.with_outliers_bf16(27, (4096, 4096))
+    q, _, s = fm.quantize(dev_bf16(big), fm.E4M3, workspace=ws)
+    assert np.array_equal(host(s).reshape(-1), oracle.quantize(big, fm.E4M3)[2].reshape(-1))
+    run(ws, "after a quantize on the same workspace")
+    run(raw[1:wsb + 1], "unaligned workspace")
+    with pytest.raises(ValueError, match="workspace needs"):
+        fm.amax(cases[0][1], fm.TENSOR, workspace=ws[: wsb - 1])
+
+
 def test_hardware_conversion_sweep():
     """fp32 inputs with scale 1 (the quotient is the input): every combination
     of sign, exponent 2^-20 .. 2^16, top 12 mantissa bits and a set of low
