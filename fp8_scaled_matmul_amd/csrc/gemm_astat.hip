@@ -196,26 +196,43 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 // soffset.  mx keeps the running maximum of the stored |bf16| patterns
 // (>= 0x7F80: an Inf or NaN was written; counted exactly at the end, see
 // recount()).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// The running maximum as it stands here, in a register: without this the
+// compiler keeps every stored word live to the end of the unit and takes
+// their maximum there, in one stretch of VALU work with the matrix pipe
+// idle.
+__device__ inline void settle(us2& m)
+{
+    uint32_t w = __builtin_bit_cast(uint32_t, m);
+    asm volatile("" : "+v"(w));
+    m = __builtin_bit_cast(us2, w);
+}
+#pragma clang diagnostic pop
+
+// The row offset goes in the lane offset, which the descriptor's range check
+// covers (the uniform offset is not range checked): rc spans the unit's
+// valid rows, so the stores of rows past the matrix are dropped, and so are
+// those of a lane whose columns are past it (voff out of range).
 template <int NF, int BF>
 __device__ inline void store_frag(const v4f (&acc)[NF][BF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
-                                  int rows, uint32_t row_bytes, float scale, us2& mx)
+                                  uint32_t row_bytes, float scale, us2& mx)
 {
     static_assert(BF == 2 || BF == 4, "unit width");
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const int rq = 4 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint32_t vo = 16 * i + rq + r < rows ? voff : gemm::kOutOfRange;
-        const int so = (16 * i + r) * (int)row_bytes;
+        const uint32_t vo = voff + (uint32_t)(16 * i + r) * row_bytes;
         const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
         mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, lo & 0x7FFF7FFFu));
         if constexpr (BF == 2) {
-            __builtin_amdgcn_raw_buffer_store_b32(lo, rc, (int)vo, so, 2);   // nontemporal
+            __builtin_amdgcn_raw_buffer_store_b32(lo, rc, (int)vo, 0, 2);   // nontemporal
         } else {
             const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
             mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, hi & 0x7FFF7FFFu));
-            __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, so, 2);   // nontemporal
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, 0, 2);   // nontemporal
         }
+        settle(mx);
     }
 }
 
@@ -475,7 +492,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         const int m0 = panel * P::rows;
         const int u_end = min(u1, (panel + 1) * p.ntn);
         if (pending) {
-            store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
+            store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), row_bytes, out_scale, mx);
             pending = false;
         }
         __syncthreads();   // every wave is done with the previous panel
@@ -495,7 +512,6 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
                 for (int f = 0; f < BF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
         }
         const __amdgpu_buffer_rsrc_t rc = out_rsrc(m0);
-        const int rows = min(P::rows, p.m - m0);
         for (; u < u_end; ++u) {
             const int n0 = (u - panel * p.ntn) * unit_cols<BF>();
             const uint32_t co = col_off(n0);
@@ -522,8 +538,8 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
                     acc[i][f] =
                         gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (s == 0 && drain) store_frag(acc, kF - 1, rc, co_prev, rows, row_bytes, out_scale, mx);
-                if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, rows, row_bytes, out_scale, mx);
+                if (s == 0 && drain) store_frag(acc, kF - 1, rc, co_prev, row_bytes, out_scale, mx);
+                if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, row_bytes, out_scale, mx);
                 __builtin_amdgcn_sched_barrier(0);
             }
             pending = true;
@@ -534,7 +550,7 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
         }
     }
     if (pending)
-        store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), min(P::rows, p.m - pm0), row_bytes, out_scale, mx);
+        store_frag(acc, kF - 1, out_rsrc(pm0), col_off(pn0), row_bytes, out_scale, mx);
     const uint32_t nonfinite = (mx.x >= 0x7F80u || mx.y >= 0x7F80u) ? recount<ROWS, BF>(p, u0, u1) : 0u;
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
     if constexpr (ASRC == 1) flush_counters_block(p.ctr, sat, und, nan);
