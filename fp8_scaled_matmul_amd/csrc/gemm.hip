@@ -100,6 +100,45 @@ __device__ inline void item_of(const KArgs& p, int bid, int& split, int& tm, int
 
 __device__ inline void tile_of(const KArgs& p, int& split, int& tm, int& tn) { item_of(p, blockIdx.x, split, tm, tn); }
 
+// Non-finite outputs: the epilogue keeps the running maximum of the stored
+// |bf16| patterns (two packed maxima per 8-byte store) and counts exactly,
+// by reading its outputs back, only when that maximum reaches the all-ones
+// exponent (an Inf or NaN was written).
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void track_max(us2& mx, uint32_t w)
+{
+    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w & 0x7FFF7FFFu));
+    // pinned here: left alone, the compiler keeps every stored word live to
+    // take their maximum after the last store
+    uint32_t v = __builtin_bit_cast(uint32_t, mx);
+    asm volatile("" : "+v"(v));
+    mx = __builtin_bit_cast(us2, v);
+}
+#pragma clang diagnostic pop
+__device__ inline bool saw_nonfinite(us2 mx) { return mx.x >= 0x7F80u || mx.y >= 0x7F80u; }
+
+// Exact count of the Inf/NaN outputs this lane stored for the tile at (m0,
+// n0) (wave w's 128 x 64 part, four adjacent columns of each of its rows per
+// lane), read back once the stores have completed.
+__device__ inline uint32_t recount_tile(const KArgs& p, int m0, int n0)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = n0 + (wave >> 1) * 64 + 4 * (lane & 15);
+    const int row0 = m0 + (wave & 1) * 128 + 4 * (lane >> 4);
+    uint32_t n = 0;
+    for (int i = 0; i < 8; ++i)
+        for (int r = 0; r < 4; ++r) {
+            const int row = row0 + 16 * i + r;
+            if (row >= p.m) continue;
+            for (int j = 0; j < 4; ++j)
+                if (col + j < p.n) n += (p.c[(int64_t)row * p.ldc + col + j] & 0x7F80u) == 0x7F80u;
+        }
+    return n;
+}
+
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_a[2 * kTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds_b[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) float g_lds_sa[4 * BM];       // s_a of 4 K blocks (ring)
@@ -450,6 +489,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             __builtin_amdgcn_make_buffer_rsrc(p.c + (int64_t)m0 * p.ldc, (short)0,
                                               (int)std::min<int64_t>(rows_c * p.ldc * 2, 0x7FFFFFF0), 0x00020000);
         const bool col_ok = col < p.n;
+        us2 mx = us2{0, 0};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -457,15 +497,14 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
                 const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
                 const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * out_scale, acc[i][1][r] * out_scale);
                 const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * out_scale, acc[i][3][r] * out_scale);
-                const bool in = col_ok && m0 + lrow < p.m;
-                // bf16 exponent all ones in any of the 4 halves
-                nonfinite += in ? (((lo & 0x7F80u) == 0x7F80u) + ((lo & 0x7F800000u) == 0x7F800000u) +
-                                   ((hi & 0x7F80u) == 0x7F80u) + ((hi & 0x7F800000u) == 0x7F800000u))
-                                : 0u;
+                // rows past m: zero accumulators (their operand rows read as zeros), stores dropped
                 const uint32_t off = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : gemm::kOutOfRange;
                 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
                 __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 2);   // nontemporal
+                track_max(mx, lo);
+                track_max(mx, hi);
             }
+        if (saw_nonfinite(mx)) nonfinite = recount_tile(p, m0, n0);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -650,7 +689,7 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
         bc = (__builtin_bit_cast(uint32_t, g_lds_sb[nbi_w]) >> 23) & 0xFFu;
     }
 
-    uint32_t nonfinite = 0;
+    us2 mx = us2{0, 0};   // over every tile's bf16 output
     for (int u = 0; c.id < total; ++u) {
         const uint8_t* la = g_lds_a + (u & 1) * kTileBytes;
         const uint8_t* la_next = g_lds_a + ((u + 1) & 1) * kTileBytes;
@@ -753,10 +792,8 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
                     const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
                     const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * out_scale, acc[i][1][r] * out_scale);
                     const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * out_scale, acc[i][3][r] * out_scale);
-                    const bool in = col_ok && m0 + lrow < p.m;
-                    nonfinite += in ? (((lo & 0x7F80u) == 0x7F80u) + ((lo & 0x7F800000u) == 0x7F800000u) +
-                                       ((hi & 0x7F80u) == 0x7F80u) + ((hi & 0x7F800000u) == 0x7F800000u))
-                                    : 0u;
+                    track_max(mx, lo);
+                    track_max(mx, hi);
                     const uint32_t off = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : gemm::kOutOfRange;
                     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
                     __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)off, 0, 2);   // nontemporal
@@ -773,6 +810,13 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block_p(KArgs p)
         fc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         pos_next(p, c);
     }
+    uint32_t nonfinite = 0;
+    if (saw_nonfinite(mx))
+        for (int id = blockIdx.x; id < total; id += gridDim.x) {
+            int split, tm, tn;
+            item_of(p, id, split, tm, tn);
+            nonfinite += recount_tile(p, tm * BM, tn * BN);
+        }
     flush_counters(p.ctr, 0, 0, 0, nonfinite);
 }
 

@@ -188,6 +188,46 @@ def test_nonfinite_output_counter():
     assert np.all((y & 0x7FFF) == 0x7F80)
 
 
+@pytest.mark.parametrize("kind", ["block_fp32", "block_pow2", "tensor_persistent"])
+def test_nonfinite_output_counter_block_kernels(kind):
+    """The block kernels keep a running maximum of the stored bf16 words and,
+    only when it reaches the all-ones exponent, read their outputs back to
+    count the Inf/NaN ones.  A few A rows of 448s times B of 448s overflow
+    with the chosen scales, one A row holds a NaN code, the other rows are
+    small and finite: the counter equals the Inf/NaN words in y, which are
+    exactly those rows.  Shapes: the block-scaled kernel (fp32 and
+    power-of-two scales, 4 tiles) and the persistent per-tensor kernel (272
+    tiles on 256 CUs, K = 2048)."""
+    g = np.random.default_rng(31)
+    if kind == "tensor_persistent":
+        m, n, k = 4352, 4096, 2048
+    else:
+        m, n, k = 512, 512, 1024
+    small = np.concatenate([np.arange(0x00, 0x39), np.arange(0x80, 0xB9)]).astype(np.uint8)   # |v| <= 1
+    a = small[g.integers(0, small.size, size=(m, k))]
+    big_rows = [3, 200, m - 1]
+    a[big_rows, :] = 0x7E                      # 448
+    a[7, k // 2] = 0x7F                        # NaN code
+    b = np.full((n, k), 0x7E, np.uint8)
+    if kind == "tensor_persistent":
+        ga, gb = fm.TENSOR, fm.TENSOR
+        sa = np.float32([1e30]).reshape(1)
+        sb = np.float32([10.0]).reshape(1)
+    else:
+        ga = fm.ROW_1x128 if kind == "block_fp32" else fm.ROW_1x128_POW2
+        gb = fm.BLOCK_128x128 if kind == "block_fp32" else fm.BLOCK_128x128_POW2
+        va, vb = (1e30, 10.0) if kind == "block_fp32" else (2.0 ** 100, 8.0)
+        sa = np.full((m, k // 128), va, np.float32)
+        sb = np.full((n // 128, k // 128), vb, np.float32)
+    ctr = fm.Counters()
+    y = host(fm.scaled_mm(dev_u8(a), fm.E4M3, dev_f32(sa), ga, dev_u8(b), fm.E4M3, dev_f32(sb), gb, counters=ctr))
+    bad = (y & 0x7F80) == 0x7F80
+    rows = np.nonzero(bad.any(axis=1))[0]
+    assert sorted(rows.tolist()) == sorted(big_rows + [7]), rows[:10]
+    assert bad[rows].all()
+    assert ctr.read()["nonfinite_out"] == int(bad.sum()) == (len(big_rows) + 1) * n
+
+
 def _check_points(y, a, fa, sa, ga, b, fb, sb, gb, g, what):
     """Every output element against the oracle GEMM on the same codes."""
     del g
