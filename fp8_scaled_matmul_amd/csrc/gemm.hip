@@ -349,7 +349,10 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
 #pragma unroll
     for (int j = 0; j < 8; ++j) block_dma_one(d, j, 1, kt0 + 1, 0, ntk > 1);
     block_dma_one(d, 8, 0, 0, kt0 + 2, ntk > 2);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // block 0's A/B and the scales of blocks 0 and 1 (older than the newest
+    // 10 instructions: block 1's 8 and the 2 of block 2's scales); block 1
+    // arrives while block 0 runs and is waited for at its slot 26
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     gemm::barrier_lds();
     if constexpr (E8M0) {
         block_codes(kt0, wave);
