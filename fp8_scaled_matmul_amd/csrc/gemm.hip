@@ -466,6 +466,24 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
     // m0 + wm + 16 i + 4 (lane/16) + r
     const int col = n0 + wn + 4 * (lane & 15);
     const int row_l = m0 + wm + 4 * (lane >> 4);
+    if (p.ws && p.fast_store) {
+        // fp32 partials: 16-byte stores through a descriptor spanning the
+        // tile's valid rows (rows past m dropped by its range check)
+        const int64_t rows_c = min(p.m - m0, BM);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            p.ws + ((int64_t)split * p.m + m0) * p.n, (short)0, (int)(rows_c * p.n * 4), 0x00020000);
+        const bool col_ok = col < p.n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lrow = wm + 16 * i + 4 * (lane >> 4) + r;
+                const uint32_t off = col_ok ? (uint32_t)((lrow * p.n + col) * 4) : gemm::kOutOfRange;
+                const v4f v = v4f{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rw, (int)off, 0, 0);
+            }
+        return;
+    }
     if (p.ws) {
         float* ws = p.ws + (int64_t)split * p.m * p.n;
 #pragma unroll
@@ -474,14 +492,9 @@ __global__ void __launch_bounds__(kBlockThreads, 1) k_gemm_block(KArgs p)
             for (int r = 0; r < 4; ++r) {
                 const int row = row_l + 16 * i + r;
                 if (row >= p.m) continue;
-                if (p.fast_store && col < p.n) {
-                    *reinterpret_cast<float4*>(&ws[(int64_t)row * p.n + col]) =
-                        float4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
-                } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (col + j < p.n) ws[(int64_t)row * p.n + col + j] = acc[i][j][r];
-                }
+                for (int j = 0; j < 4; ++j)
+                    if (col + j < p.n) ws[(int64_t)row * p.n + col + j] = acc[i][j][r];
             }
         return;
     }
