@@ -215,25 +215,30 @@ __device__ inline void settle(us2& m)
 // valid rows, so the stores of rows past the matrix are dropped, and so are
 // those of a lane whose columns are past it (voff out of range).
 template <int NF, int BF>
-__device__ inline void store_frag(const v4f (&acc)[NF][BF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
-                                  uint32_t row_bytes, float scale, us2& mx)
+__device__ inline void store_row(const v4f (&acc)[NF][BF], int i, int r, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
+                                 uint32_t row_bytes, float scale, us2& mx)
 {
     static_assert(BF == 2 || BF == 4, "unit width");
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t vo = voff + (uint32_t)(16 * i + r) * row_bytes;
-        const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, lo & 0x7FFF7FFFu));
-        if constexpr (BF == 2) {
-            __builtin_amdgcn_raw_buffer_store_b32(lo, rc, (int)vo, 0, 2);   // nontemporal
-        } else {
-            const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, hi & 0x7FFF7FFFu));
-            __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, 0, 2);   // nontemporal
-        }
-        settle(mx);
+    const uint32_t vo = voff + (uint32_t)(16 * i + r) * row_bytes;
+    const uint32_t lo = gemm::pack_bf16(acc[i][0][r] * scale, acc[i][1][r] * scale);
+    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, lo & 0x7FFF7FFFu));
+    if constexpr (BF == 2) {
+        __builtin_amdgcn_raw_buffer_store_b32(lo, rc, (int)vo, 0, 2);   // nontemporal
+    } else {
+        const uint32_t hi = gemm::pack_bf16(acc[i][2][r] * scale, acc[i][3][r] * scale);
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, hi & 0x7FFF7FFFu));
+        __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rc, (int)vo, 0, 2);   // nontemporal
     }
+    settle(mx);
+}
+
+template <int NF, int BF>
+__device__ inline void store_frag(const v4f (&acc)[NF][BF], int i, __amdgpu_buffer_rsrc_t rc, uint32_t voff,
+                                  uint32_t row_bytes, float scale, us2& mx)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_row(acc, i, r, rc, voff, row_bytes, scale, mx);
 }
 
 // The panel of rows m0 .. m0 + Panel::rows - 1 into LDS.  FP8 A: the codes are copied.
@@ -413,10 +418,10 @@ __device__ __attribute__((always_inline)) inline uint32_t recount(const AsArgs& 
 // unit at the end).  One accumulator set: in the last K step, fragment
 // i - 1 (final once its last MFMA, issued one step earlier, has run) is
 // scaled, rounded and stored at step i, and fragment F - 1 at the next
-// unit's first step, after that
-// step's MFMAs (which write fragment 0); a fragment is overwritten by the
-// next unit only after it has been read out.  A scheduling barrier closes
-// every step (and separates its MFMAs from its read-out).
+// unit's first step (whose MFMAs write fragment 0), one row after each of
+// the step's MFMAs; a fragment is overwritten by the next unit only after
+// it has been read out.  Scheduling barriers keep each step's MFMAs and
+// read-out rows in that order.
 template <int FA, int FB, int ASRC, int ROWS, int BF>
 __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
 {
@@ -512,11 +517,16 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
                 for (int f = 0; f < BF; ++f) bb[kb][f] = b_frag(rs_cur, boff, f, kb);
         }
         const __amdgpu_buffer_rsrc_t rc = out_rsrc(m0);
+        // what the panel's first unit drains (to an offset past the range)
+#pragma unroll
+        for (int f = 0; f < BF; ++f) acc[kF - 1][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         for (; u < u_end; ++u) {
             const int n0 = (u - panel * p.ntn) * unit_cols<BF>();
             const uint32_t co = col_off(n0);
-            const uint32_t co_prev = col_off(pn0);   // the previous unit of the same panel
-            const bool drain = pending;
+            // fragment kF - 1 of the previous unit of the same panel, stored at
+            // step 0; in a panel's first unit there is none, and its step 0
+            // stores zeros to an offset past the range (dropped)
+            const uint32_t co_drain = pending ? col_off(pn0) : gemm::kOutOfRange;
 #pragma unroll
             for (int s = 0; s < kAsKB * kF; ++s) {
                 const int kb = s / kF, i = s % kF;
@@ -533,14 +543,21 @@ __global__ void __launch_bounds__(kAsThreads, 1) k_gemm_astat(AsArgs p)
                     af[(s + P::ahead) % P::ring] = a_frag(ab, s3 % kF, s3 / kF);
                 }
                 const v8i& a = af[s % P::ring];
+                // a fragment's read-out goes out one row at a time between the
+                // MFMAs (4 / BF rows after each), so the VALU work runs while
+                // the matrix pipe has an MFMA to execute
 #pragma unroll
-                for (int f = 0; f < BF; ++f)
+                for (int f = 0; f < BF; ++f) {
                     acc[i][f] =
                         gemm::mfma<FA, FB>(a, bb[kb % kBRing][f], kb == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][f]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (s == 0 && drain) store_frag(acc, kF - 1, rc, co_prev, row_bytes, out_scale, mx);
-                if (kb == kAsKB - 1 && i >= 1) store_frag(acc, i - 1, rc, co, row_bytes, out_scale, mx);
-                __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = f * 4 / BF; r < (f + 1) * 4 / BF; ++r) {
+                        if (s == 0) store_row(acc, kF - 1, r, rc, co_drain, row_bytes, out_scale, mx);
+                        if (kb == kAsKB - 1 && i >= 1) store_row(acc, i - 1, r, rc, co, row_bytes, out_scale, mx);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             pending = true;
             pm0 = m0;
