@@ -200,3 +200,23 @@ def test_scaled_mm_k768_nonfinite_output_counter():
                           dev_f32(np.array([1e3], np.float32)), 0, counters=ctr))
     assert ctr.read()["nonfinite_out"] == 200 * 132
     assert np.all((y & 0x7FFF) == 0x7F80)
+
+
+def test_scaled_mm_k768_nonfinite_rows_at_panel_edges():
+    """208-row panels, 480 units of 256 columns (about two per workgroup, so a
+    unit's last fragment is stored both inside a panel and at a panel switch):
+    rows that overflow bf16 at the panel edges are counted exactly, and the
+    other rows stay zero."""
+    m, n = 208 * 40, 3072
+    a = np.zeros((m, K), np.uint8)
+    bad = [0, 191, 192, 207, 208, 415, 416, 4159, 4160, m - 1]
+    a[bad] = 0x7E
+    b = np.full((n, K), 0x7E, np.uint8)
+    ctr = fm.Counters()
+    y = host(fm.scaled_mm(dev_u8(a), 0, dev_f32(np.array([1e30], np.float32)), 0, dev_u8(b), 0,
+                          dev_f32(np.array([1e3], np.float32)), 0, counters=ctr))
+    assert ctr.read()["nonfinite_out"] == len(bad) * n
+    assert np.all((y[bad] & 0x7FFF) == 0x7F80)
+    good = np.ones(m, bool)
+    good[bad] = False
+    assert np.all(y[good] == 0)
